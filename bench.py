@@ -1,0 +1,200 @@
+"""Benchmark: packed CTC loss + gradient on one MI355X.
+
+One step = one packed_ctc_loss call (loss, mean reduction and the full (T_total, D) gradient) over
+the large-vocabulary batch: B=16 utterances, T_i uniform in [500, 3000], D=8193 (blank 0),
+U_i = round(T_i/6), float16 log probabilities, reduction mean.  Inputs are generated with a fixed
+seed and are resident in HBM before the timed region.
+
+Prints one JSON line with frames/s, the whole-call HBM rate over the counted bytes
+T_total * D * (2 bytes read + 2 bytes written), the per-kernel breakdown from HIP events recorded
+on the call's stream during the timed steps, the roofline of the dominant kernel, and the float64
+CPU oracle timed on this host's cores on the same batch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "packed CTC loss+grad frames/s and achieved HBM GB/s (% of MI355X peak)"
+HBM_PEAK_GBPS = 8000.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+DTYPE_BYTES = {"f32": 4, "bf16": 2, "f16": 2}
+
+# fp32 operations charged per state and frame of one recursion (alpha or beta): a 3-way max/med/min,
+# two subtractions, two exp2, two adds, one log2, two adds (shift and emission) -- 12 ops, each
+# transcendental counted once.  Used only when the recursion kernel is the dominant one.
+OPS_PER_STATE_STEP = 12
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="large_vocab",
+                    choices=["tiny", "small", "asr_bpe", "large_vocab", "char_level"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU-baseline leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run one device copy of 512 MiB (a known-size kernel for "
+                         "scaling hardware byte counters)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (utterances would shard across "
+              "GPUs with no exchange but a scalar all-reduce for sum/mean; see DESIGN.md). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from ctc_forward_backward_amd import api
+    from ctc_forward_backward_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    lib = api._load()
+
+    b = W.make_workload(args.workload)
+    T_total, D, B = b.T_total, b.D, b.B
+    dname = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}[b.log_probs.dtype]
+    lp = b.log_probs.to(dev)
+    cu = b.cu_seqlens.to(dev)
+    ln = b.lengths.to(dev)
+    tg = b.targets.to(dev)
+    tl = b.target_lengths.to(dev)
+    Umax = int(b.target_lengths.max())
+    W_ = int(b.targets.shape[1])
+    flags = 1 * (cu.dtype == torch.int64) | 2 * (ln.dtype == torch.int64) | 4 * (tg.dtype == torch.int64) \
+        | 8 * (tl.dtype == torch.int64)
+    ws_bytes = api.packed_ctc_workspace_size(T_total, D, B, Umax)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    losses = torch.empty(B, dtype=torch.float32, device=dev)
+    reduced = torch.empty((), dtype=torch.float32, device=dev)
+    grad = torch.empty((T_total, D), dtype=lp.dtype, device=dev)
+    red_code = api.REDUCTIONS[b.reduction]
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    call_args = (P(lp), api.DTYPE_CODES[lp.dtype], T_total, D, P(cu), P(ln), B, P(tg), W_, P(tl), flags, Umax,
+                 b.blank, int(b.zero_infinity), red_code, None, P(losses), P(reduced), P(grad), P(ws), ws_bytes, sh)
+
+    def step():
+        rc = lib.packed_ctc_loss(*call_args)
+        if rc != 0:
+            raise RuntimeError(lib.packed_ctc_last_error().decode())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    api.set_phase_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    phases = api.phase_times()
+    api.set_phase_timing(False)
+
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    elapsed = t1 - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    frames_per_s = T_total * args.steps / elapsed
+    bpe = DTYPE_BYTES[dname]
+    bytes_call = T_total * D * (bpe + bpe)
+    call_gbps = bytes_call / (ms_per_step * 1e-3) / 1e9
+
+    lengths = b.lengths.numpy().astype(np.int64)
+    S = 2 * b.target_lengths.numpy().astype(np.int64) + 1
+    state_steps = int((lengths * S).sum())
+    dominant = max(phases, key=phases.get) if phases else None
+    if dominant == "chains":
+        t = phases["chains"] * 1e-3
+        achieved = 2 * state_steps * OPS_PER_STATE_STEP / t / 1e12
+        roofline = {"bound": "alu", "kernel": "chains", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
+                    "per_launch_work": f"2 recursions x {state_steps} state-steps x {OPS_PER_STATE_STEP} fp32 ops"}
+    elif dominant is not None:
+        t = phases[dominant] * 1e-3
+        achieved = bytes_call / t / 1e9
+        roofline = {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                    "per_launch_work": f"{T_total} rows x {D} x ({bpe} B read + {bpe} B written)"}
+    else:
+        roofline = None
+
+    out = {
+        "metric": METRIC,
+        "value": frames_per_s,
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": b.name, "B": B, "T_total": T_total, "D": D, "input_dtype": dname,
+                   "max_target_length": Umax, "reduction": b.reduction, "zero_infinity": b.zero_infinity,
+                   "seed": "fixed"},
+        "call_hbm": {"achieved": call_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": call_gbps / HBM_PEAK_GBPS,
+                     "counted_bytes": bytes_call},
+        "phases_ms": phases,
+        "roofline": roofline,
+    }
+
+    if not args.no_cpu_baseline:
+        from oracle import oracle
+
+        gpu_losses = losses.cpu().double().numpy()
+        gpu_grad = grad.cpu()
+        runs, t_cpu, ref = 0, 0.0, None
+        while runs == 0 or t_cpu < args.cpu_seconds:
+            c0 = time.perf_counter()
+            ref = oracle.ctc_batch(b)
+            t_cpu += time.perf_counter() - c0
+            runs += 1
+        out["cpu_baseline"] = {
+            "value": T_total * runs / t_cpu, "unit": "frames/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"the whole {b.name} batch ({T_total} frames, D={D}), loss + gradient in float64, {runs} run(s)",
+        }
+        fin = np.isfinite(ref["loss"])
+        rel = np.abs(gpu_losses[fin] - ref["loss"][fin]) / np.maximum(np.abs(ref["loss"][fin]), 1e-30)
+        gerr = 0.0
+        for r0 in range(0, T_total, 4096):
+            g = gpu_grad[r0:r0 + 4096].double().numpy()
+            rg = ref["grad"][r0:r0 + 4096]
+            ok = ~np.isnan(rg)
+            if ok.any():
+                gerr = max(gerr, float(np.max(np.abs(g[ok] - rg[ok]))))
+        out["parity_vs_oracle"] = {"loss_max_rel_err": float(rel.max()) if rel.size else 0.0,
+                                   "grad_max_abs_err": gerr}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

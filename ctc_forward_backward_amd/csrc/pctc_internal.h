@@ -1,0 +1,201 @@
+// Internal declarations of the packed CTC HIP library (gfx950 only).
+//
+// Data flow of one packed_ctc_loss call, all on the caller's stream:
+//   prep      per utterance: clamp metadata, extended-label ids, row -> utterance map
+//   gather    per owned row: the U+1 distinct emissions log2 p(blank), log2 p(l_1..l_U) of that row,
+//             shifted by an integer per-row offset so that they sit near 0
+//   chains    one workgroup per (utterance, direction): the alpha and the beta recursions run
+//             concurrently in one launch, each frame renormalised by the previous frame's maximum
+//   weights   per utterance: loss, zero_infinity, gradient weight; the sum / mean reduction
+//   dense     per owned row: posteriors as a per-frame softmax over states of alpha + beta - lp,
+//             summed per class in LDS, then one coalesced pass writing w*exp(lp) - posterior
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pctc {
+
+// log-space "minus infinity": finite so that max-based log-sum-exp never forms inf - inf
+constexpr float kNeg = -1.0e30f;
+constexpr float kNegHalf = -5.0e29f;  // values below this carry no probability mass
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kLn2 = 0.6931471805599453;
+
+constexpr int kMaxTargetLength = 8191;  // S = 2U+1 <= 16383 states per utterance
+constexpr int kMaxClasses = 32768;      // per-class posterior accumulator in LDS (128 KB)
+
+enum Dtype { kF32 = 0, kBF16 = 1, kF16 = 2 };
+
+struct Meta {
+  int start;  // first row
+  int T;      // frames (clamped so that rows stay inside the buffer)
+  int U;      // labels (clamped to the workspace bound)
+  int flags;  // bit 0: a NaN log probability was gathered
+};
+
+// Workspace carve-up.  Every region is 256-byte aligned.
+// Frames per chunk of the recursions: their prefetch depth and the period of their integer shift.
+// A block's offset is stored once per chunk, at the row of the chunk's first frame.
+constexpr int kChunk = 16;
+
+// Rows of padding before and after the emission table: the recursions prefetch up to two chunks
+// of frames past either end of an utterance without clamping.
+constexpr int kEPad = 40;
+
+struct Layout {
+  int64_t T_total, D, B, Umax;
+  int64_t E_stride;  // floats per row of the emission table (>= Umax + 1)
+  int64_t Gmax;      // state-pair blocks of the longest target: ceil((Umax + 1) / 64)
+  size_t off_meta, off_lab, off_rowmap, off_rowoff, off_E, off_AB, off_nll, off_llb, off_w, off_ring, off_nring,
+      off_sig, off_items, off_ctl, total;
+};
+
+// control words of the recursion work queue
+struct ChainCtl {
+  int qlen;    // number of queued blocks
+  int qcount;  // next block to claim
+  int err;     // non-zero: a block gave up waiting for its neighbour (results unspecified)
+  int pad[61];
+};
+
+Layout make_layout(int64_t T_total, int64_t D, int64_t B, int64_t Umax);
+
+struct Pointers {
+  Meta* meta;
+  int* lab;      // (B, Umax + 1): j = 0 the blank, j >= 1 targets[b][j-1]
+  int* rowmap;   // (T_total,): owning utterance or -1
+  int* rowoff;   // (T_total,): integer offset subtracted from the row's gathered log2 emissions
+  float* E;      // (T_total, E_stride), kEPad rows of padding on either side
+  // (2, Gmax, T_total, 128): normalised log2 alpha (direction 0) and beta (direction 1) per block
+  // of 64 state pairs and per row.  Alpha pair k sits at 2k, 2k+1 (states 2k, 2k+1); beta pair k at
+  // 2k, 2k+1 (states 2k-1, 2k), i.e. beta of state s at position s+1, all relative to the block.
+  float* AB;
+  double* nll;   // (B,) raw negative log-likelihood in nats (+inf: no alignment)
+  double* llb;   // (B,) log2 likelihood from the beta side (consistency check)
+  float* w;      // (B,) gradient weight
+  unsigned long long* ring;  // (2, Gmax, T_total) block-boundary values (value, offset) per frame
+  unsigned long long* nring; // (T_total,) (-inf, 0) in every slot: the neighbour of an edge block
+  int* sig;      // (2, Gmax, T_total) integer offset of each block's stored values, per chunk
+  int* items;    // (2 B Gmax) queued recursion blocks: (utterance * 2 + direction) << 12 | block
+  ChainCtl* ctl;
+};
+
+Pointers carve(void* workspace, const Layout& L);
+
+// ---- device helpers ----------------------------------------------------------------------------
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+// log2(2^a + 2^b) with the finite sentinel: the result stays at the sentinel when both are.
+__device__ __forceinline__ float lse2(float a, float b) {
+  const float hi = fmaxf(a, b), lo = fminf(a, b);
+  return hi + log2_fast(1.0f + exp2_fast(lo - hi));
+}
+
+// log2(2^a + 2^b + 2^c)
+__device__ __forceinline__ float lse3(float a, float b, float c) {
+  const float hi = fmaxf(fmaxf(a, b), c);
+  const float lo = fminf(fminf(a, b), c);
+  const float mid = __builtin_amdgcn_fmed3f(a, b, c);
+  return hi + log2_fast(1.0f + exp2_fast(mid - hi) + exp2_fast(lo - hi));
+}
+
+__device__ __forceinline__ float load_lp(const void* p, int dtype, int64_t i) {
+  if (dtype == kF32) return static_cast<const float*>(p)[i];
+  if (dtype == kF16) return static_cast<float>(static_cast<const _Float16*>(p)[i]);
+  const uint32_t bits = static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16;
+  return __builtin_bit_cast(float, bits);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);  // quiet NaN
+  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ void store_grad(void* p, int dtype, int64_t i, float v) {
+  if (dtype == kF32) {
+    static_cast<float*>(p)[i] = v;
+  } else if (dtype == kF16) {
+    static_cast<_Float16*>(p)[i] = static_cast<_Float16>(v);
+  } else {
+    static_cast<uint16_t*>(p)[i] = f32_to_bf16_rne(v);
+  }
+}
+
+__device__ __forceinline__ int64_t load_index(const void* p, bool i64, int64_t i) {
+  return i64 ? static_cast<const int64_t*>(p)[i] : static_cast<int64_t>(static_cast<const int32_t*>(p)[i]);
+}
+
+// DPP lane moves (gfx9 encodings): row_shr:n = 0x110 + n, row_bcast:15 = 0x142, row_bcast:31 = 0x143,
+// wave_shr:1 = 0x138, wave_shl:1 = 0x130.  Lanes without a source, and rows outside ROWS, keep `old`.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_f32(float old, float src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, src),
+                                                               CTRL, ROWS, 0xf, false));
+}
+
+// maximum over the 64 lanes of a wave, returned to every lane
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f32<0x111>(kNeg, x));
+  x = fmaxf(x, dpp_f32<0x112>(kNeg, x));
+  x = fmaxf(x, dpp_f32<0x114>(kNeg, x));
+  x = fmaxf(x, dpp_f32<0x118>(kNeg, x));
+  x = fmaxf(x, dpp_f32<0x142, 0xa>(kNeg, x));  // row r (r = 1, 3) takes lane 15 of row r-1
+  x = fmaxf(x, dpp_f32<0x143, 0xc>(kNeg, x));  // rows 2, 3 take lane 31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+// sum over the 64 lanes of a wave, returned to every lane
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_f32<0x111>(0.0f, x);
+  x += dpp_f32<0x112>(0.0f, x);
+  x += dpp_f32<0x114>(0.0f, x);
+  x += dpp_f32<0x118>(0.0f, x);
+  x += dpp_f32<0x142, 0xa>(0.0f, x);
+  x += dpp_f32<0x143, 0xc>(0.0f, x);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+// Workgroup barrier that orders LDS accesses only: global loads and stores stay in flight across it
+// (a full __syncthreads() is a workgroup fence over every address space and drains them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ---- launchers (each in its own translation unit) ----------------------------------------------
+
+struct Inputs {
+  const void* log_probs;
+  int dtype;
+  int64_t T_total, D;
+  const void* cu_seqlens;
+  const void* lengths;
+  int64_t B;
+  const void* targets;
+  int64_t target_width;
+  const void* target_lengths;
+  int index_flags;
+  int blank;
+  int zero_infinity;
+  int reduction;
+  const float* grad_scale;
+};
+
+hipError_t launch_prep(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
+hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
+hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
+hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
+hipError_t launch_weights(const Inputs& in, const Layout& L, const Pointers& P, float* losses_out, float* reduced_out,
+                          hipStream_t s);
+hipError_t launch_dense(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s);
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+hipError_t launch_zero_bytes(void* p, int64_t nbytes, hipStream_t s);
+hipError_t launch_reduce(const float* losses, const void* target_lengths, bool i64, int64_t B, int reduction, float* out,
+                         hipStream_t s);
+
+}  // namespace pctc

@@ -1,0 +1,283 @@
+// Per-utterance preparation, the emission gather, loss finalisation and reductions.
+//
+// Method: NVIDIA-NeMo/Speech pull request "feat(asr): native CTC loss kernel over sequence-packed log
+// probabilities", Triton file: `_extended_labels` (state s is the blank for even s and
+// targets[b][(s-1)/2] for odd s), `_frame_log_probs` (the per-frame log probabilities at the states'
+// classes, computed in float32), `_PackedCTCLoss.forward` (zero_infinity on the loss) and
+// `_beta_grad_kernel` (the gradient scale, zero under zero_infinity for an infinite loss); `ctc.py`
+// `forward_packed` (sum, and the mean of each loss over its clamped target length, then the batch mean).
+#include "pctc_internal.h"
+
+namespace pctc {
+
+namespace {
+
+__global__ void fill_i32_kernel(int* p, int64_t n, int v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+__global__ void fill_u64_kernel(unsigned long long* p, int64_t n, unsigned long long v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+__global__ void fill_f32_kernel(float* p, int64_t n, float v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+__global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+__global__ void zero_u8_kernel(uint8_t* p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+// One workgroup per utterance: clamp the metadata so that every later access stays in bounds,
+// write the U+1 distinct class ids of the extended label sequence, claim the utterance's rows.
+__global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers P) {
+  const int b = blockIdx.x;
+  __shared__ Meta m;
+  if (threadIdx.x == 0) {
+    int64_t start = load_index(in.cu_seqlens, in.index_flags & 1, b);
+    int64_t T = load_index(in.lengths, in.index_flags & 2, b);
+    int64_t U = load_index(in.target_lengths, in.index_flags & 8, b);
+    if (T < 0) T = 0;
+    if (start < 0 || start > L.T_total) {
+      start = 0;
+      T = 0;
+    }
+    if (T > L.T_total - start) T = L.T_total - start;
+    if (U < 0) U = 0;
+    if (U > L.Umax) U = L.Umax;
+    if (U > in.target_width) U = in.target_width;
+    m.start = static_cast<int>(start);
+    m.T = static_cast<int>(T);
+    m.U = static_cast<int>(U);
+    m.flags = 0;
+    P.meta[b] = m;
+  }
+  __syncthreads();
+  const Meta mm = m;
+  int* lab = P.lab + (int64_t)b * (L.Umax + 1);
+  const bool t64 = in.index_flags & 4;
+  for (int j = threadIdx.x; j <= mm.U; j += blockDim.x) {
+    int64_t c = in.blank;
+    if (j > 0) {
+      c = load_index(in.targets, t64, (int64_t)b * in.target_width + (j - 1));
+      if (c < 0) c = 0;
+      if (c >= L.D) c = L.D - 1;
+    }
+    lab[j] = static_cast<int>(c);
+  }
+  for (int t = threadIdx.x; t < mm.T; t += blockDim.x) P.rowmap[mm.start + t] = b;
+}
+
+// One wave per owned row: the log2 emissions of the row at the utterance's U+1 distinct classes,
+// minus the row's integer offset floor(max), so that the recursions work on values near 0.
+__global__ void __launch_bounds__(256) gather_kernel(Inputs in, Layout L, Pointers P) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= L.T_total) return;
+  const int b = P.rowmap[r];
+  if (b < 0) return;
+  const int U = P.meta[b].U;
+  const int* lab = P.lab + (int64_t)b * (L.Umax + 1);
+  const int64_t base = r * L.D;
+  float mx = kNeg;
+  int nan = 0;
+  for (int j = lane; j <= U; j += 64) {
+    float v = load_lp(in.log_probs, in.dtype, base + lab[j]) * kLog2e;
+    nan |= (v != v);
+    v = fmaxf(v, kNeg);  // -inf (and NaN, flagged above) become the finite sentinel
+    mx = fmaxf(mx, v);
+  }
+  mx = wave_max(mx);
+  const float off = mx > kNegHalf ? floorf(mx) : 0.0f;
+  float* E = P.E + r * L.E_stride;
+  for (int j = lane; j <= U; j += 64) {
+    float v = fmaxf(load_lp(in.log_probs, in.dtype, base + lab[j]) * kLog2e, kNeg);
+    E[j] = v - off;
+  }
+  if (lane == 0) P.rowoff[r] = static_cast<int>(off);
+  if (nan) atomicOr(&P.meta[b].flags, 1);
+}
+
+// Losses after zero_infinity, gradient weights and the sum / mean reduction (one workgroup,
+// a fixed summation tree so that the reduced value is reproducible).
+__global__ void __launch_bounds__(256) weights_kernel(Inputs in, Layout L, Pointers P, float* losses_out,
+                                                      float* reduced_out) {
+  __shared__ double part[256];
+  double acc = 0.0;
+  const int64_t B = L.B;
+  for (int64_t b = threadIdx.x; b < B; b += blockDim.x) {
+    const double nll = P.nll[b];
+    const bool inf = nll == (double)INFINITY;
+    const double loss = (in.zero_infinity && inf) ? 0.0 : nll;
+    if (losses_out) losses_out[b] = static_cast<float>(loss);
+    // the target length of the reductions is the caller's value, as the page's reductions divide by it
+    int64_t U = load_index(in.target_lengths, in.index_flags & 8, b);
+    const double Uc = U > 1 ? (double)U : 1.0;
+    double w = in.grad_scale ? (double)in.grad_scale[b] : 1.0;
+    if (in.reduction == 2) w /= (double)B * Uc;
+    if (in.zero_infinity && inf) w = 0.0;
+    P.w[b] = static_cast<float>(w);
+    acc += in.reduction == 2 ? loss / Uc : loss;
+  }
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if (threadIdx.x < h) part[threadIdx.x] += part[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0 && reduced_out && in.reduction != 0) {
+    double v = part[0];
+    if (in.reduction == 2) v = B > 0 ? v / (double)B : (double)NAN;
+    *reduced_out = static_cast<float>(v);
+  }
+}
+
+__global__ void __launch_bounds__(256) reduce_kernel(const float* losses, const void* tl, bool i64, int64_t B,
+                                                     int reduction, float* out) {
+  __shared__ double part[256];
+  double acc = 0.0;
+  for (int64_t b = threadIdx.x; b < B; b += blockDim.x) {
+    const int64_t U = load_index(tl, i64, b);
+    acc += reduction == 2 ? (double)losses[b] / (U > 1 ? (double)U : 1.0) : (double)losses[b];
+  }
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if (threadIdx.x < h) part[threadIdx.x] += part[threadIdx.x + h];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    double v = part[0];
+    if (reduction == 2) v = B > 0 ? v / (double)B : (double)NAN;
+    *out = static_cast<float>(v);
+  }
+}
+
+// Work queue of the recursions (one workgroup).  Utterances are ordered by frame count, longest
+// first, so that the longest chains start first; each utterance contributes its alpha segments
+// (four 64-pair state blocks each) in producer order (segment 0 first) interleaved with its beta
+// segments in producer order (last segment first).  A segment only ever waits on its producer,
+// which sits earlier in the queue, so segments claimed in queue order can always finish.
+// Frameless utterances get their loss here.
+__global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, int sort) {
+  extern __shared__ int sh[];  // sort ? [T (B) | order (B)] : unused
+  const int B = static_cast<int>(L.B);
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if (sort) {
+    int* sT = sh;
+    int* order = sh + B;
+    for (int b = tid; b < B; b += nt) sT[b] = P.meta[b].T;
+    __syncthreads();
+    for (int b = tid; b < B; b += nt) {
+      const int Tb = sT[b];
+      int rank = 0;
+      for (int c = 0; c < B; ++c) {
+        const int Tc = sT[c];
+        if (Tc > Tb || (Tc == Tb && c < b)) ++rank;
+      }
+      order[rank] = b;
+    }
+    __syncthreads();
+  }
+  for (int b = tid; b < B; b += nt) {
+    const Meta m = P.meta[b];
+    if (m.T == 0) {
+      P.nll[b] = m.U == 0 ? 0.0 : (double)INFINITY;
+      P.llb[b] = m.U == 0 ? 0.0 : -(double)INFINITY;
+    }
+  }
+  if (tid == 0) {
+    int n = 0;
+    for (int i = 0; i < B; ++i) {
+      const int b = sort ? sh[B + i] : i;
+      const Meta m = P.meta[b];
+      if (m.T == 0) continue;
+      // segments of four 64-pair blocks
+      const int nseg = (((m.U + 1 + 63) >> 6) + 3) >> 2;
+      for (int j = 0; j < nseg; ++j) {
+        P.items[n++] = ((2 * b) << 12) | j;
+        P.items[n++] = ((2 * b + 1) << 12) | (nseg - 1 - j);
+      }
+    }
+    P.ctl->qlen = n;
+    P.ctl->qcount = 0;
+    P.ctl->err = 0;
+  }
+}
+
+int grid_for(int64_t n, int threads) {
+  int64_t g = (n + threads - 1) / threads;
+  if (g > 4096) g = 4096;
+  return g < 1 ? 1 : static_cast<int>(g);
+}
+
+}  // namespace
+
+hipError_t launch_prep(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {
+  if (L.T_total > 0) {
+    fill_i32_kernel<<<grid_for(L.T_total, 256), 256, 0, s>>>(P.rowmap, L.T_total, -1);
+  }
+  if (L.B > 0) prep_kernel<<<static_cast<unsigned>(L.B), 256, 0, s>>>(in, L, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {
+  if (L.T_total > 0 && L.B > 0) {
+    const int64_t blocks = (L.T_total + 3) / 4;
+    gather_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(in, L, P);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {
+  (void)in;
+  if (L.B == 0) return hipGetLastError();
+  // every ring slot starts empty (all ones); a block publishes (value, offset) into it once
+  const int64_t words = 2 * 2 * L.Gmax * L.T_total;
+  if (words > 0) fill_i32_kernel<<<grid_for(words, 256), 256, 0, s>>>(reinterpret_cast<int*>(P.ring), words, -1);
+  // the neighbour of an edge block: (-inf, offset 0) in every slot
+  const unsigned long long none = (unsigned long long)__builtin_bit_cast(uint32_t, kNeg);
+  if (L.T_total > 0) fill_u64_kernel<<<grid_for(L.T_total, 256), 256, 0, s>>>(P.nring, L.T_total, none);
+  const int sort = L.B <= 8192 ? 1 : 0;
+  const size_t lds = sort ? 2 * sizeof(int) * (size_t)L.B : 0;
+  if (lds > 48 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&schedule_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  schedule_kernel<<<1, 1024, lds, s>>>(L, P, sort);
+  return hipGetLastError();
+}
+
+hipError_t launch_weights(const Inputs& in, const Layout& L, const Pointers& P, float* losses_out, float* reduced_out,
+                          hipStream_t s) {
+  weights_kernel<<<1, 256, 0, s>>>(in, L, P, losses_out, reduced_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+  if (n > 0) fill_f32_kernel<<<grid_for(n, 256), 256, 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_bytes(void* p, int64_t nbytes, hipStream_t s) {
+  if (nbytes <= 0) return hipGetLastError();
+  if ((reinterpret_cast<uintptr_t>(p) & 3) == 0 && (nbytes & 3) == 0) {
+    zero_u32_kernel<<<grid_for(nbytes / 4, 256), 256, 0, s>>>(static_cast<uint32_t*>(p), nbytes / 4);
+  } else {
+    zero_u8_kernel<<<grid_for(nbytes, 256), 256, 0, s>>>(static_cast<uint8_t*>(p), nbytes);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const float* losses, const void* target_lengths, bool i64, int64_t B, int reduction, float* out,
+                         hipStream_t s) {
+  reduce_kernel<<<1, 256, 0, s>>>(losses, target_lengths, i64, B, reduction, out);
+  return hipGetLastError();
+}
+
+}  // namespace pctc

@@ -1,0 +1,161 @@
+/*
+ * packed_ctc.h — CTC loss and gradient over sequence-packed log probabilities on MI355X (gfx950).
+ *
+ * The operation is the one defined on the NVIDIA-NeMo/Speech pull request page "feat(asr): native
+ * CTC loss kernel over sequence-packed log probabilities" ([PR] below): the public function
+ * `packed_ctc_loss` of its Triton file, its two kernels `_alpha_kernel` / `_beta_grad_kernel`, its
+ * autograd backward, and the reductions of `forward_packed` in its `ctc.py` diff.
+ *
+ * Layout (the token-flat packing of [PR], module description and `packed_ctc_loss` arguments):
+ *   log_probs  (T_total, D) row-major, float32 / bfloat16 / float16, the blank among the D classes.
+ *              Utterance b owns rows [cu_seqlens[b], cu_seqlens[b] + lengths[b]).  Rows owned by no
+ *              utterance (gaps, trailing rows) get a zero gradient.
+ *   cu_seqlens (B + 1,) int32 or int64 first row of each utterance (entry B is not read).
+ *   lengths    (B,)     int32 or int64 frames per utterance.
+ *   targets    (B, target_width) int32 or int64 row-major, label ids in [0, D); only the first
+ *              target_lengths[b] entries of row b are read (the rest may hold anything).
+ *              A target equal to the blank id is an ordinary label ([PR] `_alpha_kernel`).
+ *   target_lengths (B,) int32 or int64.
+ *
+ * All pointers except the stream are DEVICE pointers owned by the caller.  Calls are asynchronous
+ * on `stream` (a hipStream_t passed as void*; NULL = the default stream) and allocate nothing: all
+ * scratch lives in the caller's `workspace`.  No call keeps a pointer after it returns.
+ * Every function returns PCTC_OK (0) or one of the error codes below; on error nothing has been
+ * launched and packed_ctc_last_error() holds a message (thread-local).
+ */
+#ifndef PACKED_CTC_H
+#define PACKED_CTC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* log_probs / grad dtypes ([PR] `PACKED_CTC_LOSS_DTYPES`: float32, bfloat16, float16; float64 is
+ * rejected by the kernel) */
+#define PCTC_DTYPE_F32 0
+#define PCTC_DTYPE_BF16 1
+#define PCTC_DTYPE_F16 2
+
+/* index_flags: a set bit makes that array int64, a clear bit int32 */
+#define PCTC_I64_CU_SEQLENS 1
+#define PCTC_I64_LENGTHS 2
+#define PCTC_I64_TARGETS 4
+#define PCTC_I64_TARGET_LENGTHS 8
+
+/* reductions of [PR] `forward_packed`: none, sum, and the mean of each loss over its clamped
+ * target length max(U_b, 1), then the batch mean */
+#define PCTC_REDUCTION_NONE 0
+#define PCTC_REDUCTION_SUM 1
+#define PCTC_REDUCTION_MEAN 2
+
+/* error codes, one per failure class of [PR] `packed_ctc_loss` argument checks */
+#define PCTC_OK 0
+#define PCTC_ERR_SHAPE 1              /* a size is negative or inconsistent (the page's ValueError on shapes) */
+#define PCTC_ERR_DTYPE 2              /* log_probs dtype not F32/BF16/F16 (the page's TypeError) */
+#define PCTC_ERR_BLANK 3              /* blank outside [0, D) */
+#define PCTC_ERR_NEG_TARGET_LENGTH 4  /* a negative target length (checked on the host read) */
+#define PCTC_ERR_TARGET_LENGTH_WIDTH 5/* a target length beyond target_width (checked on the host read) */
+#define PCTC_ERR_WORKSPACE 6          /* workspace missing or smaller than packed_ctc_workspace_size() */
+#define PCTC_ERR_HIP 7                /* a HIP runtime or launch error */
+#define PCTC_ERR_ARG 8                /* a required pointer is NULL, or an unknown flag / reduction */
+#define PCTC_ERR_LIMIT 9              /* beyond what this build supports (see packed_ctc_limits) */
+
+/*
+ * Bytes of device workspace packed_ctc_loss needs for T_total frames, D classes, B utterances and
+ * target lengths up to max_target_length.  Returns 0 for negative arguments.
+ */
+size_t packed_ctc_workspace_size(int64_t T_total, int64_t D, int64_t B, int64_t max_target_length);
+
+/*
+ * Supported maxima of this build: the longest target (labels) and the class count D.
+ * Either pointer may be NULL.
+ */
+void packed_ctc_limits(int64_t* max_target_length, int64_t* max_classes);
+
+/*
+ * Host-synchronous read of target_lengths ([PR] `packed_ctc_loss`: the host check of the padded
+ * kernel, no negative length and none beyond the targets width, and the longest target sizes the
+ * states).  Copies the B lengths to the host on `stream`, waits, and stores their maximum (0 when
+ * B = 0) in *max_out.  Errors: PCTC_ERR_NEG_TARGET_LENGTH, PCTC_ERR_TARGET_LENGTH_WIDTH.
+ * Must not be called while `stream` is being captured into a graph.
+ */
+int packed_ctc_max_target_length(const void* target_lengths, int index_flags, int64_t B, int64_t target_width,
+                                 void* stream, int64_t* max_out);
+
+/*
+ * CTC loss per utterance and its gradient ([PR] `packed_ctc_loss`, `_PackedCTCLoss`, the kernels).
+ *
+ * Computes, per utterance b with T = lengths[b] frames and U = target_lengths[b] labels over the
+ * extended label sequence blank, l1, blank, ..., lU, blank (S = 2U + 1 states):
+ *   nll_b = -log(sum over alignments) by the log-space alpha recursion; T = 0 gives 0 when U = 0
+ *           and +inf otherwise; no alignment gives +inf;
+ *   losses_out[b] = nll_b, or 0 when zero_infinity and nll_b = +inf          (B floats, fp32);
+ *   reduced_out   = sum_b losses_out[b] (SUM) or mean_b losses_out[b] / max(U_b, 1) (MEAN);
+ *                   not written for NONE; may be NULL;
+ *   grad_out      = (T_total, D) in the dtype of log_probs, round-to-nearest-even:
+ *                   w_b * (exp(log_probs) - posterior summed per class) on the rows of utterance b,
+ *                   0 on rows owned by no utterance.  This is the gradient with respect to the
+ *                   logits of a log_softmax ([PR] module description).  w_b is
+ *                   (grad_scale ? grad_scale[b] : 1) times 1/(B * max(U_b, 1)) for MEAN, and 0
+ *                   when zero_infinity and nll_b = +inf.  An infeasible utterance with w_b != 0
+ *                   gets NaN in every column of its rows.  May be NULL (loss only).
+ *
+ * max_target_length >= 0: a caller-promised bound on every target length (no host read; the call
+ *   is then graph-capturable).  Lengths beyond it, negative lengths, label ids outside [0, D), or
+ *   utterance rows outside [0, T_total) are precondition violations: the kernels clamp them so
+ *   that every memory access stays in bounds, and the results for that utterance are unspecified.
+ * max_target_length < 0: the library reads target_lengths on the host exactly as
+ *   packed_ctc_max_target_length does, except while `stream` is being captured, where
+ *   target_width stands in ([PR] `packed_ctc_loss`: no host read under graph capture).
+ * The workspace must be at least packed_ctc_workspace_size(T_total, D, B, bound) bytes, bound =
+ *   max_target_length if >= 0 else target_width, and 256-byte aligned.
+ * Rows of different utterances must not overlap.  Inputs are read only; outputs are fully written.
+ */
+int packed_ctc_loss(const void* log_probs, int dtype, int64_t T_total, int64_t D, const void* cu_seqlens,
+                    const void* lengths, int64_t B, const void* targets, int64_t target_width,
+                    const void* target_lengths, int index_flags, int64_t max_target_length, int blank,
+                    int zero_infinity, int reduction, const float* grad_scale, float* losses_out, float* reduced_out,
+                    void* grad_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Reduction of per-utterance losses ([PR] `ctc.py` `forward_packed`): SUM = sum of losses[b];
+ * MEAN = mean over b of losses[b] / max(target_lengths[b], 1); B = 0 gives 0 (SUM) or NaN (MEAN).
+ * Writes one float to *out (device).  NONE is PCTC_ERR_ARG.  Only the target-length bit of
+ * index_flags is read.
+ */
+int packed_ctc_reduce(const float* losses, const void* target_lengths, int index_flags, int64_t B, int reduction,
+                      float* out, void* stream);
+
+/*
+ * Health word of the last packed_ctc_loss call that used this workspace.  The recursions of one
+ * utterance run as a pipeline of blocks that wait on each other with a bounded spin; a block that
+ * gives up sets a flag and the results of that call are unspecified.  Waits for `stream`, then
+ * stores 0 (healthy) or non-zero in *status_out.
+ */
+int packed_ctc_workspace_status(const void* workspace, void* stream, int* status_out);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* packed_ctc_last_error(void);
+
+/* Library version string. */
+const char* packed_ctc_version(void);
+
+/*
+ * Measurement hook.  While enabled, packed_ctc_loss records a HIP event before and after each of
+ * its kernels on the call's stream, for up to the last 128 calls.  Enabling (or disabling) resets
+ * the record.  packed_ctc_phase_times waits for the last recorded call and writes up to n
+ * (name, mean milliseconds over the recorded calls) pairs; it returns the number of phases, 0 if
+ * none were recorded, or minus an error code.  Names are static strings.  Not thread-safe and not
+ * for use under graph capture.
+ */
+int packed_ctc_set_phase_timing(int enable);
+int packed_ctc_phase_times(const char** names, float* ms, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PACKED_CTC_H */

@@ -1,0 +1,245 @@
+"""HIP path vs the float64 oracle, element by element, through the C ABI.
+
+Tolerances: losses within 1e-4 relative for float32 inputs and 2e-3 for bfloat16 / float16 inputs;
+gradients within 1e-4 / 2e-3 absolute (the gradient is stored in the input dtype, so for bfloat16 /
+float16 the rounding of the stored value is part of the budget).  Several results are correct where
+the method sums repeated labels in any order; the comparison is tolerance-based throughout.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from ctc_forward_backward_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: (1e-4, 1e-4), torch.bfloat16: (2e-3, 2e-3), torch.float16: (2e-3, 2e-3)}
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ctc_forward_backward_amd import api as _api
+
+    _api._load()
+    return _api
+
+
+def run_gpu(api, batch, *, reduction=None, grad_scale=None, need_grad=True, max_target_length=None,
+            index_dtypes=None, cpu_targets=False):
+    dev = torch.device("cuda:0")
+    cu, ln, tg, tl = batch.cu_seqlens, batch.lengths, batch.targets, batch.target_lengths
+    if index_dtypes is not None:
+        cu, ln, tg, tl = (x.to(d) for x, d in zip((cu, ln, tg, tl), index_dtypes))
+    if not cpu_targets:
+        tg, tl = tg.to(dev), tl.to(dev)
+    losses, reduced, grad = api.packed_ctc_loss(
+        batch.log_probs.to(dev), cu.to(dev), ln.to(dev), tg, tl, blank=batch.blank,
+        zero_infinity=batch.zero_infinity, reduction=batch.reduction if reduction is None else reduction,
+        grad_scale=grad_scale, need_grad=need_grad, max_target_length=max_target_length)
+    torch.cuda.synchronize()
+    assert api.last_call_status() == 0, "a recursion block gave up waiting for its neighbour"
+    return {
+        "loss": losses.cpu().double().numpy(),
+        "reduced": None if reduced is None else float(reduced.cpu()),
+        "grad": None if grad is None else grad.cpu().double().numpy(),
+        "grad_dtype": None if grad is None else grad.dtype,
+    }
+
+
+def compare(got, ref, dtype, label=""):
+    lrt, gat = TOL[dtype]
+    loss, rloss = got["loss"], ref["loss"]
+    assert loss.shape == rloss.shape
+    inf_ref = np.isinf(rloss)
+    assert np.array_equal(np.isinf(loss), inf_ref), label
+    fin = ~inf_ref
+    np.testing.assert_allclose(loss[fin], rloss[fin], rtol=lrt, atol=1e-5, err_msg=label)
+    if ref.get("reduced") is not None and got.get("reduced") is not None:
+        np.testing.assert_allclose(got["reduced"], ref["reduced"], rtol=lrt, atol=1e-6, err_msg=label)
+    if got.get("grad") is not None:
+        g, rg = got["grad"], ref["grad"]
+        nan_ref = np.isnan(rg)
+        assert np.array_equal(np.isnan(g), nan_ref), label
+        ok = ~nan_ref
+        err = np.abs(g[ok] - rg[ok])
+        worst = float(err.max()) if err.size else 0.0
+        _say(f"  {label}: max |grad err| = {worst:.3e} (tol {gat}), max loss rel err = "
+             f"{float(np.max(np.abs(loss[fin] - rloss[fin]) / np.maximum(np.abs(rloss[fin]), 1e-30))) if fin.any() else 0:.3e}")
+        assert worst <= gat, f"{label}: gradient error {worst} > {gat}"
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "asr_bpe", "large_vocab", "char_level"])
+def test_workload_full_size(api, oracle_mod, name):
+    _say(f"[gpu parity] workload {name}")
+    b = W.make_workload(name)
+    got = run_gpu(api, b)
+    ref = oracle_mod.ctc_batch(b)
+    compare(got, ref, b.log_probs.dtype, name)
+    assert got["grad_dtype"] == b.log_probs.dtype
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
+def test_dtypes_and_reductions(api, oracle_mod, dtype, reduction):
+    _say(f"[gpu parity] dtype {dtype} reduction {reduction}")
+    rng = np.random.default_rng(11)
+    lengths = [int(x) for x in rng.integers(1, 300, size=9)] + [0]
+    tl = [int(rng.integers(0, max(1, T // 3) + 1)) for T in lengths]
+    tl[-1] = 0
+    targets = [[int(x) for x in rng.integers(1, 200, size=u)] for u in tl]
+    b = W.make_batch(lengths, targets, 200, seed=5, sigma=2.5, dtype=dtype, reduction=reduction)
+    compare(run_gpu(api, b), oracle_mod.ctc_batch(b), b.log_probs.dtype, f"{dtype}/{reduction}")
+
+
+def test_grad_scale(api, oracle_mod):
+    b = W.tiny()
+    gs = torch.tensor([0.5, -2.0, 0.0, 3.0])
+    for red in ("none", "mean"):
+        got = run_gpu(api, b, reduction=red, grad_scale=gs)
+        ref = oracle_mod.ctc_batch(b, reduction=red, grad_scale=gs.numpy())
+        compare(got, ref, torch.float32, f"grad_scale/{red}")
+
+
+def test_page_structures(api, oracle_mod):
+    # the structures of the packed kernel page's tests, with our own seeded values
+    cases = [
+        ("small case", W.make_batch([8, 5, 2], [[1, 1, 2], [2], []], 5, seed=7, blank=4)),
+        ("repeats and blank-id labels", W.make_batch([9, 9, 7], [[1, 1, 2, 2], [4, 4, 1], [2, 4, 2]], 5, seed=3,
+                                                     blank=4)),
+        ("empty targets", W.make_batch([6, 3], [[], []], 3, seed=5, blank=2)),
+        ("production shape", W.make_batch([667, 401, 123, 50, 599, 300],
+                                          [list(np.random.default_rng(13).integers(0, 1026, size=T // 6))
+                                           for T in [667, 401, 123, 50, 599, 300]], 1027, seed=13, blank=1026,
+                                          reduction="mean")),
+        ("last target is the blank id", W.make_batch([12, 7], [[3, 1, 0], [0]], 4, seed=2, blank=0)),
+    ]
+    for label, b in cases:
+        _say(f"[gpu parity] {label}")
+        compare(run_gpu(api, b), oracle_mod.ctc_batch(b), torch.float32, label)
+
+
+@pytest.mark.parametrize("zero_infinity", [False, True])
+def test_zero_length_and_impossible(api, oracle_mod, zero_infinity):
+    _say(f"[gpu parity] zero-length / impossible, zero_infinity={zero_infinity}")
+    b = W.make_batch([5, 0, 3, 1, 6], [[1, 2], [1], [2], [1, 1], [2, 2, 2]], 4, seed=11, blank=3,
+                     zero_infinity=zero_infinity)
+    got = run_gpu(api, b)
+    ref = oracle_mod.ctc_batch(b)
+    compare(got, ref, torch.float32, "zero-length/impossible")
+    assert got["loss"][1] == (0.0 if zero_infinity else math.inf)
+    assert got["loss"][3] == (0.0 if zero_infinity else math.inf)  # T=1 with a repeat: no alignment
+    if zero_infinity:
+        assert np.all(got["grad"][8:9] == 0.0)
+
+
+def test_over_allocated_targets_fillers_and_gaps(api, oracle_mod):
+    _say("[gpu parity] over-allocated targets, fillers, gaps")
+    tight = W.make_batch([9, 7, 4], [[1, 2, 3, 1], [2, 2, 4], [4, 1]], 6, seed=17, blank=5)
+    wide = W.make_batch([9, 7, 4, 0, 0], [[1, 2, 3, 1], [2, 2, 4], [4, 1], [], []], 6, seed=17, blank=5, width=32,
+                        gaps=[2, 3, 0, 1, 0], T_total=30)
+    a = run_gpu(api, tight)
+    g = run_gpu(api, wide)
+    compare(g, oracle_mod.ctc_batch(wide), torch.float32, "wide")
+    assert np.all(g["loss"][3:] == 0.0)
+    owned = np.zeros(30, dtype=bool)
+    for b in range(3):
+        r0 = int(wide.cu_seqlens[b])
+        owned[r0:r0 + int(wide.lengths[b])] = True
+    assert np.all(g["grad"][~owned] == 0.0)
+    # same utterances, same values -> same losses whether the width is 4 or 32
+    tight2 = W.make_batch([9, 7, 4], [[1, 2, 3, 1], [2, 2, 4], [4, 1]], 6, seed=17, blank=5, width=32)
+    tight2.log_probs = tight.log_probs.clone()  # the junk draw shifts the generator; reuse the values
+    np.testing.assert_allclose(run_gpu(api, tight2)["loss"], a["loss"], rtol=1e-6)
+
+
+@pytest.mark.parametrize("dt", [(torch.int32,) * 4, (torch.int64,) * 4, (torch.int32, torch.int64, torch.int32,
+                                                                          torch.int64)])
+def test_index_dtypes_and_cpu_targets(api, oracle_mod, dt):
+    b = W.tiny()
+    ref = oracle_mod.ctc_batch(b)
+    compare(run_gpu(api, b, index_dtypes=dt), ref, torch.float32, f"index {dt}")
+    compare(run_gpu(api, b, index_dtypes=dt, cpu_targets=True), ref, torch.float32, "cpu targets")
+
+
+def test_long_targets_multiple_pairs_per_lane(api, oracle_mod):
+    # U up to 3000 -> more than 1024 state pairs per utterance, several pairs per lane
+    _say("[gpu parity] long targets")
+    rng = np.random.default_rng(8)
+    lengths = [6500, 3100, 40]
+    tl = [3000, 1500, 10]
+    targets = [[int(x) for x in rng.integers(1, 64, size=u)] for u in tl]
+    b = W.make_batch(lengths, targets, 64, seed=8, sigma=2.0, reduction="mean")
+    compare(run_gpu(api, b), oracle_mod.ctc_batch(b), torch.float32, "long targets")
+
+
+def test_large_vocabulary_lds_accumulator(api, oracle_mod):
+    _say("[gpu parity] D = 30000")
+    rng = np.random.default_rng(9)
+    lengths = [200, 120]
+    targets = [[int(x) for x in rng.integers(0, 29999, size=u)] for u in (40, 25)]
+    b = W.make_batch(lengths, targets, 30000, seed=9, sigma=3.0, dtype="bf16", blank=29999, reduction="sum")
+    compare(run_gpu(api, b), oracle_mod.ctc_batch(b), torch.bfloat16, "D=30000")
+
+
+def test_loss_only_and_explicit_bound(api, oracle_mod):
+    b = W.small()
+    ref = oracle_mod.ctc_batch(b, want_grad=False)
+    got = run_gpu(api, b, need_grad=False, max_target_length=int(b.target_lengths.max()))
+    assert got["grad"] is None
+    compare(got, ref, torch.float32, "loss only")
+    # a looser caller bound gives the same result
+    got2 = run_gpu(api, b, need_grad=False, max_target_length=int(b.targets.shape[1]))
+    np.testing.assert_allclose(got2["loss"], got["loss"], rtol=1e-6)
+
+
+def test_host_read_errors(api):
+    b = W.tiny()
+    dev = torch.device("cuda:0")
+    args = (b.log_probs.to(dev), b.cu_seqlens.to(dev), b.lengths.to(dev), b.targets.to(dev))
+    with pytest.raises(ValueError, match="negative"):
+        api.packed_ctc_loss(*args, torch.tensor([3, -1, 2, 2], device=dev), blank=0)
+    with pytest.raises(ValueError, match="targets width"):
+        api.packed_ctc_loss(*args, b.target_lengths.to(dev) + 100, blank=0)
+    with pytest.raises(TypeError, match="float32"):
+        api.packed_ctc_loss(b.log_probs.double().to(dev), *args[1:], b.target_lengths.to(dev), blank=0)
+    with pytest.raises(ValueError, match="blank"):
+        api.packed_ctc_loss(*args, b.target_lengths.to(dev), blank=16)
+
+
+def test_reduce_entry_point(api):
+    dev = torch.device("cuda:0")
+    losses = torch.tensor([1.0, 4.0, 9.0], device=dev)
+    tl = torch.tensor([0, 2, 3], device=dev)
+    assert abs(float(api.packed_ctc_reduce(losses, tl, "sum")) - 14.0) < 1e-6
+    assert abs(float(api.packed_ctc_reduce(losses, tl, "mean")) - (1.0 + 2.0 + 3.0) / 3) < 1e-6
+    empty = api.packed_ctc_reduce(torch.zeros(0, device=dev), torch.zeros(0, dtype=torch.long, device=dev), "mean")
+    assert math.isnan(float(empty))
+
+
+def test_empty_batch(api):
+    dev = torch.device("cuda:0")
+    lp = torch.randn(7, 4, device=dev).log_softmax(-1)
+    losses, red, grad = api.packed_ctc_loss(lp, torch.zeros(1, dtype=torch.int32, device=dev),
+                                            torch.zeros(0, dtype=torch.long, device=dev),
+                                            torch.zeros(0, 3, dtype=torch.long, device=dev),
+                                            torch.zeros(0, dtype=torch.long, device=dev), blank=0, reduction="sum")
+    torch.cuda.synchronize()
+    assert losses.numel() == 0 and float(red) == 0.0
+    assert torch.all(grad == 0)
+
+
+def test_repeatable_within_tolerance(api):
+    b = W.asr_bpe()
+    a = run_gpu(api, b)
+    c = run_gpu(api, b)
+    np.testing.assert_allclose(a["loss"], c["loss"], rtol=1e-6)
+    np.testing.assert_allclose(np.nan_to_num(a["grad"]), np.nan_to_num(c["grad"]), atol=2e-3)

@@ -290,8 +290,9 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
 
   // the first chunk is peeled so that the loop starts from the same memory-counter state it
   // leaves with, and the compiler's waits do not drain the stores and loads in flight
-  if (more) run_chunk(0);
-  for (int c = 1; more; ++c) run_chunk(c);
+  int c = 0;
+  if (more) run_chunk(c++);
+  while (more) run_chunk(c++);
 
   // ---- likelihood: the block holding the last states (alpha) or the first states (beta) ----
   const bool owner = BETA ? (cx.j == 0) : (cx.j == (U >> 6));
@@ -315,6 +316,7 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
     if (!BETA) {
       const bool nan = P.meta[cx.b].flags & 1;
       P.nll[cx.b] = nan ? (double)NAN : (feasible ? -log2p * kLn2 : (double)INFINITY);
+      P.lsh[cx.b] = (double)off + (double)fin;
     } else {
       P.llb[cx.b] = feasible ? log2p : -(double)INFINITY;
     }

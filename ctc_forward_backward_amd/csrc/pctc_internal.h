@@ -47,7 +47,8 @@ struct Layout {
   int64_t T_total, D, B, Umax;
   int64_t E_stride;  // floats per row of the emission table (>= Umax + 1)
   int64_t Gmax;      // state-pair blocks of the longest target: ceil((Umax + 1) / 64)
-  size_t off_meta, off_lab, off_rowmap, off_rowoff, off_E, off_AB, off_nll, off_llb, off_w, off_ring, off_nring,
+  int64_t Dw;        // 32-bit words of a class bitmap: ceil(D / 32)
+  size_t off_cbits, off_cpref, off_dmap, off_meta, off_lab, off_rowmap, off_rowoff, off_E, off_AB, off_nll, off_llb, off_lsh, off_w, off_ring, off_nring,
       off_sig, off_items, off_ctl, total;
 };
 
@@ -73,12 +74,17 @@ struct Pointers {
   float* AB;
   double* nll;   // (B,) raw negative log-likelihood in nats (+inf: no alignment)
   double* llb;   // (B,) log2 likelihood from the beta side (consistency check)
+  double* lsh;   // (B,) log2 likelihood from the alpha side without the row offsets
   float* w;      // (B,) gradient weight
   unsigned long long* ring;  // (2, Gmax, T_total) block-boundary values (value, offset) per frame
   unsigned long long* nring; // (T_total,) (-inf, 0) in every slot: the neighbour of an edge block
   int* sig;      // (2, Gmax, T_total) integer offset of each block's stored values, per chunk
   int* items;    // (2 B Gmax) queued recursion blocks: (utterance * 2 + direction) << 12 | block
   ChainCtl* ctl;
+  // classes of each utterance's extended labels (blank and labels), for the gradient rows:
+  uint32_t* cbits;  // (B, Dw) bitmap of the classes present
+  int* cpref;       // (B, Dw) number of classes present in the words before each word
+  int* dmap;        // (B, Umax + 1) rank among the present classes of lab[j]
 };
 
 Pointers carve(void* workspace, const Layout& L);
@@ -127,6 +133,113 @@ __device__ __forceinline__ void store_grad(void* p, int dtype, int64_t i, float 
 
 __device__ __forceinline__ int64_t load_index(const void* p, bool i64, int64_t i) {
   return i64 ? static_cast<const int64_t*>(p)[i] : static_cast<int64_t>(static_cast<const int32_t*>(p)[i]);
+}
+
+// ---- 8-element chunks of a (T_total, D) log-prob / gradient buffer ----------------------------
+// Chunk q holds flat elements [8q, 8q+8): 16 aligned bytes for 16-bit dtypes, 32 for float32.
+
+// Raw bytes of one chunk, held while its load is in flight.
+template <int DT>
+struct Raw8 {
+  uint4 u[DT == kF32 ? 2 : 1];
+};
+
+template <int DT>
+__device__ __forceinline__ Raw8<DT> ld8(const void* base, int64_t q) {
+  Raw8<DT> r;
+  if constexpr (DT == kF32) {
+    const uint4* p = static_cast<const uint4*>(base) + 2 * q;
+    r.u[0] = p[0];
+    r.u[1] = p[1];
+  } else {
+    r.u[0] = static_cast<const uint4*>(base)[q];
+  }
+  return r;
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack8(const Raw8<DT>& r, float v[8]) {
+  if constexpr (DT == kF32) {
+    const uint32_t w[8] = {r.u[0].x, r.u[0].y, r.u[0].z, r.u[0].w, r.u[1].x, r.u[1].y, r.u[1].z, r.u[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __builtin_bit_cast(float, w[i]);
+  } else {
+    const uint32_t w[4] = {r.u[0].x, r.u[0].y, r.u[0].z, r.u[0].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == kF16) {
+        v[2 * i] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i] & 0xffffu)));
+        v[2 * i + 1] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i] >> 16)));
+      } else {
+        v[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+        v[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+      }
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store8(void* base, int64_t q, const float v[8]) {
+  if constexpr (DT == kF32) {
+    float4* p = static_cast<float4*>(base) + 2 * q;
+    p[0] = make_float4(v[0], v[1], v[2], v[3]);
+    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t lo, hi;
+      if constexpr (DT == kF16) {
+        lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[2 * i]));
+        hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v[2 * i + 1]));
+      } else {
+        lo = f32_to_bf16_rne(v[2 * i]);
+        hi = f32_to_bf16_rne(v[2 * i + 1]);
+      }
+      w[i] = lo | (hi << 16);
+    }
+    static_cast<uint4*>(base)[q] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// Visit the flat elements [f0, f1) of a (T_total, D) buffer with one wave: aligned 8-element
+// chunks in the middle and single elements (fn1(element)) at the ragged ends; nothing outside
+// [f0, f1) is touched.  With a source buffer, up to kBatch chunks per lane are loaded before any is
+// used (fn8(chunk index, first element, values)), so a wave keeps that many loads in flight;
+// without one (src == nullptr) fn8 gets no values.
+constexpr int kBatch = 8;
+
+template <int DT, typename F8, typename F1>
+__device__ __forceinline__ void wave_segment(const void* src, int64_t f0, int64_t f1, int lane, F8 fn8, F1 fn1) {
+  int64_t a0 = (f0 + 7) & ~int64_t(7), a1 = f1 & ~int64_t(7);
+  if (a0 > a1) a0 = a1 = f1;  // shorter than one aligned chunk: all single elements
+  if (f0 + lane < a0) fn1(f0 + lane);
+  const int64_t qe = a1 >> 3;
+  for (int64_t q0 = (a0 >> 3) + lane; q0 < qe; q0 += 64 * kBatch) {
+    if (src) {
+      Raw8<DT> raw[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (q0 + 64 * u < qe) raw[u] = ld8<DT>(src, q0 + 64 * u);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (q0 + 64 * u < qe) {
+          float v[8];
+          unpack8<DT>(raw[u], v);
+          fn8(q0 + 64 * u, (q0 + 64 * u) << 3, v);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (q0 + 64 * u < qe) {
+          float v[8];
+          fn8(q0 + 64 * u, (q0 + 64 * u) << 3, v);
+        }
+      }
+    }
+  }
+  if (a1 + lane < f1 && a1 + lane >= a0) fn1(a1 + lane);
 }
 
 // DPP lane moves (gfx9 encodings): row_shr:n = 0x110 + n, row_bcast:15 = 0x142, row_bcast:31 = 0x143,
@@ -192,6 +305,7 @@ hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P,
 hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
 hipError_t launch_weights(const Inputs& in, const Layout& L, const Pointers& P, float* losses_out, float* reduced_out,
                           hipStream_t s);
+hipError_t launch_classes(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
 hipError_t launch_dense(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 hipError_t launch_zero_bytes(void* p, int64_t nbytes, hipStream_t s);

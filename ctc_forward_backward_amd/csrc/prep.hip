@@ -74,32 +74,105 @@ __global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers
 
 // One wave per owned row: the log2 emissions of the row at the utterance's U+1 distinct classes,
 // minus the row's integer offset floor(max), so that the recursions work on values near 0.
+// The row is staged through LDS in tiles with aligned 16-byte loads (the label columns are
+// scattered over the row, and reading them one by one would fetch a whole sector each).
+constexpr int kGTile = 4096;  // elements of a row per LDS tile (one tile per wave)
+
+template <int DT>
 __global__ void __launch_bounds__(256) gather_kernel(Inputs in, Layout L, Pointers P) {
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (r >= L.T_total) return;
-  const int b = P.rowmap[r];
-  if (b < 0) return;
+  extern __shared__ float gsm[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float* tile = gsm + wave * (kGTile + 8);
+  const int64_t D = L.D;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + wave; r < L.T_total; r += (int64_t)gridDim.x * 4) {
+    const int b = P.rowmap[r];
+    if (b < 0) continue;
+    const int U = P.meta[b].U;
+    const int* lab = P.lab + (int64_t)b * (L.Umax + 1);
+    float* E = P.E + r * L.E_stride;
+    float mx = kNeg;
+    int nan = 0;
+    for (int64_t t0 = 0; t0 < D; t0 += kGTile) {
+      const int64_t f0 = r * D + t0, f1 = f0 + min((int64_t)kGTile, D - t0);
+      const int64_t base = f0 & ~int64_t(7);  // tile[f - base] holds element f; chunks land 8-aligned
+      wave_segment<DT>(
+          in.log_probs, f0, f1, lane,
+          [&](int64_t, int64_t f, const float* v) {
+            float4* t = reinterpret_cast<float4*>(tile + (f - base));
+            t[0] = make_float4(v[0], v[1], v[2], v[3]);
+            t[1] = make_float4(v[4], v[5], v[6], v[7]);
+          },
+          [&](int64_t f) { tile[f - base] = load_lp(in.log_probs, DT, f); });
+      // the tile was written by this wave's lanes; LDS operations of one wave complete in order
+      for (int j = lane; j <= U; j += 64) {
+        const int64_t c = lab[j];
+        if (c >= t0 && c < t0 + kGTile) {
+          float v = tile[r * D + c - base] * kLog2e;
+          nan |= (v != v);
+          v = fmaxf(v, kNeg);  // -inf (and NaN, flagged above) become the finite sentinel
+          mx = fmaxf(mx, v);
+          E[j] = v;
+        }
+      }
+    }
+    mx = wave_max(mx);
+    const float off = mx > kNegHalf ? floorf(mx) : 0.0f;
+    for (int j = lane; j <= U; j += 64) E[j] -= off;
+    if (lane == 0) P.rowoff[r] = static_cast<int>(off);
+    if (nan) atomicOr(&P.meta[b].flags, 1);
+  }
+}
+
+// One workgroup per utterance: the bitmap of the classes its extended labels use (the blank and
+// its labels), the number of classes before each bitmap word, and for each label index j the rank
+// of lab[j] among the present classes.  The gradient rows add each class's posterior at its
+// column through these ranks.
+__global__ void __launch_bounds__(256) classes_kernel(Layout L, Pointers P) {
+  extern __shared__ uint32_t cw[];  // Dw bitmap words, then Dw prefix counts
+  __shared__ int wsum[4];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int Dw = static_cast<int>(L.Dw);
   const int U = P.meta[b].U;
   const int* lab = P.lab + (int64_t)b * (L.Umax + 1);
-  const int64_t base = r * L.D;
-  float mx = kNeg;
-  int nan = 0;
-  for (int j = lane; j <= U; j += 64) {
-    float v = load_lp(in.log_probs, in.dtype, base + lab[j]) * kLog2e;
-    nan |= (v != v);
-    v = fmaxf(v, kNeg);  // -inf (and NaN, flagged above) become the finite sentinel
-    mx = fmaxf(mx, v);
+  for (int i = tid; i < Dw; i += 256) cw[i] = 0u;
+  __syncthreads();
+  for (int j = tid; j <= U; j += 256) atomicOr(&cw[lab[j] >> 5], 1u << (lab[j] & 31));
+  __syncthreads();
+  uint32_t* gbits = P.cbits + (int64_t)b * Dw;
+  int* gpref = P.cpref + (int64_t)b * Dw;
+  // exclusive prefix count of set bits over the words, 256 words at a time
+  int carry = 0;
+  for (int w0 = 0; w0 < Dw; w0 += 256) {
+    const int i = w0 + tid;
+    const uint32_t bits = i < Dw ? cw[i] : 0u;
+    int v = __builtin_popcount(bits);
+    // inclusive scan within the wave
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(v, o);
+      if (lane >= o) v += t;
+    }
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    int before = carry;
+    for (int k = 0; k < wave; ++k) before += wsum[k];
+    if (i < Dw) {
+      const int pref = before + v - __builtin_popcount(bits);
+      gbits[i] = bits;
+      gpref[i] = pref;
+      cw[Dw + i] = static_cast<uint32_t>(pref);
+    }
+    carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
   }
-  mx = wave_max(mx);
-  const float off = mx > kNegHalf ? floorf(mx) : 0.0f;
-  float* E = P.E + r * L.E_stride;
-  for (int j = lane; j <= U; j += 64) {
-    float v = fmaxf(load_lp(in.log_probs, in.dtype, base + lab[j]) * kLog2e, kNeg);
-    E[j] = v - off;
+  __syncthreads();
+  // rank of each label's class
+  int* dmap = P.dmap + (int64_t)b * (L.Umax + 1);
+  for (int j = tid; j <= U; j += 256) {
+    const int c = lab[j], wi = c >> 5;
+    dmap[j] = static_cast<int>(cw[Dw + wi]) + __builtin_popcount(cw[wi] & ((1u << (c & 31)) - 1u));
   }
-  if (lane == 0) P.rowoff[r] = static_cast<int>(off);
-  if (nan) atomicOr(&P.meta[b].flags, 1);
 }
 
 // Losses after zero_infinity, gradient weights and the sum / mean reduction (one workgroup,
@@ -226,10 +299,36 @@ hipError_t launch_prep(const Inputs& in, const Layout& L, const Pointers& P, hip
 }
 
 hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {
-  if (L.T_total > 0 && L.B > 0) {
-    const int64_t blocks = (L.T_total + 3) / 4;
-    gather_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(in, L, P);
+  if (L.T_total == 0 || L.B == 0) return hipGetLastError();
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t want = (L.T_total + 3) / 4;
+  const int grid = static_cast<int>(want < 2 * (int64_t)cus ? want : 2 * (int64_t)cus);
+  const size_t lds = 4 * (kGTile + 8) * sizeof(float);
+  auto launch = [&](auto kernel) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (err != hipSuccess) return err;
+    kernel<<<grid, 256, lds, s>>>(in, L, P);
+    return hipGetLastError();
+  };
+  if (in.dtype == kF32) return launch(&gather_kernel<kF32>);
+  if (in.dtype == kF16) return launch(&gather_kernel<kF16>);
+  return launch(&gather_kernel<kBF16>);
+}
+
+hipError_t launch_classes(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {
+  (void)in;
+  if (L.B == 0) return hipGetLastError();
+  const size_t lds = 2 * sizeof(uint32_t) * (size_t)L.Dw;
+  if (lds > 48 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&classes_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
   }
+  classes_kernel<<<static_cast<unsigned>(L.B), 256, lds, s>>>(L, P);
   return hipGetLastError();
 }
 

@@ -112,6 +112,7 @@ int packed_ctc_max_target_length(const void* target_lengths, int index_flags, in
  *   target_width stands in ([PR] `packed_ctc_loss`: no host read under graph capture).
  * The workspace must be at least packed_ctc_workspace_size(T_total, D, B, bound) bytes, bound =
  *   max_target_length if >= 0 else target_width, and 256-byte aligned.
+ * log_probs and grad_out must be 16-byte aligned (PCTC_ERR_ARG otherwise).
  * Rows of different utterances must not overlap.  Inputs are read only; outputs are fully written.
  */
 int packed_ctc_loss(const void* log_probs, int dtype, int64_t T_total, int64_t D, const void* cu_seqlens,

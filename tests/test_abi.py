@@ -97,6 +97,8 @@ def _call(**kw):
     (dict(cu=None), api.ERR_ARG, "required"),
     (dict(losses=None), api.ERR_ARG, "required"),
     (dict(targets=None), api.ERR_ARG, "targets"),
+    (dict(log_probs=ctypes.c_void_p(0x1008)), api.ERR_ARG, "aligned"),
+    (dict(grad=ctypes.c_void_p(0x1004)), api.ERR_ARG, "aligned"),
     (dict(maxU=9000, W=9000), api.ERR_LIMIT, "limit"),
     (dict(D=40000, grad=ctypes.c_void_p(0x1000)), api.ERR_LIMIT, "limit"),
     (dict(ws=None, ws_bytes=0), api.ERR_WORKSPACE, "workspace"),

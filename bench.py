@@ -34,6 +34,43 @@ DTYPE_BYTES = {"f32": 4, "bf16": 2, "f16": 2}
 OPS_PER_STATE_STEP = 12
 
 
+PHASE_KERNELS = {"chains": "chain_workers", "dense": "dense_kernel", "gather": "gather_kernel"}
+
+
+def kernel_sources_sha() -> str:
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "ctc_forward_backward_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(workload: str, phase: str):
+    """HBM bytes per launch of a phase's kernel from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary (already scaled by the copy calibration); None when there is no summary or the kernel
+    sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_bytes_{workload}.txt")
+    if not os.path.exists(path) or phase not in PHASE_KERNELS:
+        return None
+    sha, rows = None, {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("source_sha = "):
+                sha = line.split("=", 1)[1].strip()
+            parts = line.split()
+            if len(parts) == 5 and parts[0].startswith(PHASE_KERNELS[phase]):
+                try:
+                    rows[parts[0]] = (float(parts[3]) + float(parts[4])) * 1e6
+                except ValueError:
+                    pass
+    if sha != kernel_sources_sha() or len(rows) != 1:
+        return None
+    return next(iter(rows.values()))
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,14 +170,17 @@ def main():
     if dominant == "chains":
         t = phases["chains"] * 1e-3
         achieved = 2 * state_steps * OPS_PER_STATE_STEP / t / 1e12
+        t_max = int(lengths.max())
         roofline = {"bound": "alu", "kernel": "chains", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
-                    "per_launch_work": f"2 recursions x {state_steps} state-steps x {OPS_PER_STATE_STEP} fp32 ops"}
+                    "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
+                    "traffic": profiled_traffic(b.name, "chains"),
+                    "per_launch_work": f"2 recursions x {state_steps} state-steps x {OPS_PER_STATE_STEP} fp32 ops",
+                    "critical_path": {"frames": t_max, "ns_per_frame": t * 1e9 / t_max}}
     elif dominant is not None:
         t = phases[dominant] * 1e-3
         achieved = bytes_call / t / 1e9
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                    "frac": achieved / HBM_PEAK_GBPS, "traffic": profiled_traffic(b.name, dominant),
                     "per_launch_work": f"{T_total} rows x {D} x ({bpe} B read + {bpe} B written)"}
     else:
         roofline = None

@@ -16,12 +16,21 @@
 //     (2k-1, 2k) = (label k, blank) for beta.  Either way a lane needs one value per frame from
 //     outside its pair, the label of the neighbouring pair, moved one lane by DPP (wave_shr:1 for
 //     alpha, wave_shl:1 for beta).
-//   - Between blocks that value flows one way (alpha: block j-1 -> j; beta: j+1 -> j).  Four
-//     consecutive blocks form a segment run by the four waves of one workgroup (one per SIMD):
-//     inside a segment the edge value goes through a 64-slot LDS ring, tagged with its frame;
-//     between segments through a global ring slot per frame (one 64-bit system-scope store into a
-//     slot that starts empty).  Nobody waits on a later block, so the pipeline has no round trip
-//     per frame, only a fill latency per block.  An edge block reads a ring that holds -inf.
+//   - Per pair and frame the step is two two-way log-sum-exps: t = lse(blank, neighbour) gives the
+//     new blank, and lse(label, skip allowed ? t : blank) the new label (the three-way sum of the
+//     label state is the two-way sum of the label with t).  A label state that does not exist reads
+//     an emission column that holds -1e30, so it stays far below every real state and needs no
+//     mask; the lanes past the last pair only feed lanes that do not exist either.
+//   - Between blocks the neighbour value flows one way (alpha: block j-1 -> j; beta: j+1 -> j).
+//     Four consecutive blocks form a segment run by the four waves of one workgroup (one per SIMD):
+//     inside a segment the edge value goes through a 128-slot LDS ring, between segments through a
+//     global ring slot per frame (one 64-bit system-scope store into a slot that starts at zero).
+//     A slot holds the value and, in its high word, the producer's integer offset and a validity
+//     mark (the LDS ring also tags the chunk, since its slots are reused).  Nobody waits on a later
+//     block, so the pipeline has no round trip per frame, only a fill latency per block.
+//   - A consumer takes the neighbour values of a whole 16-frame chunk at the chunk's start, one per
+//     lane, checks them with one ballot and converts them to its own offset; a frame then costs one
+//     v_readlane.  Global slots are loaded one chunk ahead.
 //   - Segments are items of one work queue, producers first (see the schedule kernel), claimed by
 //     a persistent grid: a claimed segment's producer is always already running.  Every wait is
 //     bounded; a wave that gives up raises ctl->err and continues, so the kernel always ends.
@@ -29,13 +38,11 @@
 //     emissions carry an integer per-row offset, and each block shifts its values by an integer
 //     (its maximum) every chunk, so stored values stay near 0; the offsets are stored per
 //     (block, chunk) and summed in float64 for the loss.
-//   - Per frame a wave issues one 512-byte store of its 128 states (a block-major time series, so
-//     the address moves by a constant) and one edge value, both unconditional.
-//   - Emissions and global neighbour values are prefetched a 16-frame chunk ahead: the blank
-//     emission and the global slot one frame per lane (read back with v_readlane), the lane's own
-//     label emission in a ring of 16 registers, each reloaded right after its use.  Loads and
-//     stores share one in-order counter on this GPU, so the loop keeps fewer than 64 of them in
-//     flight and starts (first chunk peeled) from the state it ends with.
+//   - Per frame a wave issues one 512-byte store of its 128 states (a block-major time series) and
+//     one load of next chunk's label emission, both through buffer resources rebased per chunk so
+//     that every offset is a scalar register; the blank emission of a chunk is one load per lane.
+#include <type_traits>
+
 #include "pctc_internal.h"
 
 namespace pctc {
@@ -43,11 +50,14 @@ namespace pctc {
 namespace {
 
 constexpr int kK = kChunk;             // frames per chunk (prefetch depth and renormalisation period)
-constexpr int kR = 64;                 // LDS ring slots per wave boundary
+constexpr int kR = 128;                // LDS ring slots per wave boundary (8 chunks)
 constexpr int kWaves = 4;              // blocks per segment = waves per workgroup
-constexpr unsigned long long kEmpty = ~0ull;
 constexpr int kSpinLimit = 1 << 20;    // polls before a wave gives up waiting (about a second)
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
 static_assert(2 * kK + 1 <= kEPad, "emission padding must cover two chunks of prefetch");
+static_assert(kR % kK == 0, "a chunk's ring slots must not wrap");
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ unsigned long long gload(const unsigned long long* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -65,30 +75,22 @@ __device__ __forceinline__ void lstore(unsigned long long* p, unsigned long long
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-__device__ __forceinline__ unsigned long long pack_global(float v, float off) {
-  return (unsigned long long)__builtin_bit_cast(uint32_t, v) |
-         ((unsigned long long)__builtin_bit_cast(uint32_t, off) << 32);
+// high word of a ring slot: integer offset << 8 | 0x80 (written) | producer chunk & 127
+// (chunk -1 is the first frame)
+__device__ __forceinline__ uint32_t slot_hi(float off, int chunk) {
+  return (static_cast<uint32_t>(static_cast<int>(off)) << 8) | 0x80u | (static_cast<uint32_t>(chunk) & 127u);
 }
 
-// LDS slot: value | (integer offset << 8 | 0x80 | frame & 127) -- the tag tells this frame's entry
-// from the one 64 frames earlier and from a cleared slot (tag 0)
-__device__ __forceinline__ uint32_t lds_tag(int step) { return 0x80u | (static_cast<uint32_t>(step) & 127u); }
-
-__device__ __forceinline__ unsigned long long pack_lds(float v, float off, int step) {
-  const uint32_t hi = (static_cast<uint32_t>(static_cast<int>(off)) << 8) | lds_tag(step);
+__device__ __forceinline__ unsigned long long pack(float v, uint32_t hi) {
   return (unsigned long long)__builtin_bit_cast(uint32_t, v) | ((unsigned long long)hi << 32);
 }
 
-__device__ __forceinline__ unsigned long long uniform64(unsigned long long v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-  return (unsigned long long)lo | ((unsigned long long)hi << 32);
-}
+__device__ __forceinline__ uint32_t slot_hi_of(unsigned long long v) { return static_cast<uint32_t>(v >> 32); }
 
-__device__ __forceinline__ unsigned long long lane64(unsigned long long v, int i) {
-  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), i);
-  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), i);
-  return (unsigned long long)lo | ((unsigned long long)hi << 32);
+// the slot's value in the frame of a reader whose offset is `off`
+__device__ __forceinline__ float slot_value(unsigned long long v, float off) {
+  const int o = static_cast<int>(slot_hi_of(v)) >> 8;
+  return __builtin_bit_cast(float, static_cast<uint32_t>(v)) + (static_cast<float>(o) - off);
 }
 
 __device__ __forceinline__ float lanef(float v, int i) {
@@ -103,38 +105,51 @@ __device__ __forceinline__ bool gave_up(int* err) {
   return __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0;
 }
 
-// bounded wait for a global ring slot; on give-up the neighbour value is -inf
-__device__ __noinline__ unsigned long long wait_global(const unsigned long long* p, int* err) {
-  unsigned long long v = uniform64(gload(p));
+// chunk of the frame at `step` (chunk c holds steps 1 + c*kK .. (c+1)*kK; step 0 is chunk -1)
+__device__ __forceinline__ int chunk_of(int step) { return step == 0 ? -1 : (step - 1) / kK; }
+
+__device__ __forceinline__ bool global_ok(unsigned long long v) { return (slot_hi_of(v) & 0x80u) != 0; }
+
+__device__ __forceinline__ bool lds_ok(unsigned long long v, int chunk) {
+  return (slot_hi_of(v) & 0xffu) == (0x80u | (static_cast<uint32_t>(chunk) & 127u));
+}
+
+// Bounded wait until every lane that `needs` it holds a written global slot (each lane re-reads
+// its own slot); on give-up the missing values are -inf at offset 0.  The waits are inline: a call
+// in the frame loop would make the compiler drain every load and store in flight at each chunk.
+__device__ __forceinline__ unsigned long long wait_global(const unsigned long long* p, unsigned long long v, bool need,
+                                                       int* err) {
   int spins = 0;
-  while (v == kEmpty) {
+  while (__ballot(need && !global_ok(v))) {
     if (++spins > kSpinLimit || gave_up(err)) {
       give_up(err);
-      return pack_global(kNeg, 0.0f);
+      if (need && !global_ok(v)) v = pack(kNeg, 0x80u);
+      break;
     }
     __builtin_amdgcn_s_sleep(2);
-    v = uniform64(gload(p));
+    if (need && !global_ok(v)) v = gload(p);
   }
   return v;
 }
 
-// bounded wait for the LDS ring slot of frame `step`
-__device__ __noinline__ unsigned long long wait_lds(unsigned long long* p, int step, int* err) {
-  unsigned long long v = uniform64(lload(p));
+// the same for LDS slots tagged with the chunk each lane expects
+__device__ __forceinline__ unsigned long long wait_lds(const unsigned long long* p, unsigned long long v, bool need,
+                                                    int chunk, int* err) {
   int spins = 0;
-  while (((v >> 32) & 0xffu) != lds_tag(step)) {
+  while (__ballot(need && !lds_ok(v, chunk))) {
     if (++spins > kSpinLimit || gave_up(err)) {
       give_up(err);
-      return pack_lds(kNeg, 0.0f, step);
+      if (need && !lds_ok(v, chunk)) v = pack(kNeg, 0x80u | (static_cast<uint32_t>(chunk) & 127u));
+      break;
     }
     __builtin_amdgcn_s_sleep(1);
-    v = uniform64(lload(p));
+    if (need && !lds_ok(v, chunk)) v = lload(p);
   }
   return v;
 }
 
-// bounded wait until the consumer wave has finished chunk `c`
-__device__ __noinline__ void wait_progress(int* prog, int c, int* err) {
+// bounded wait until the consumer wave has taken the neighbour values of chunk `c`
+__device__ __forceinline__ void wait_progress(int* prog, int c, int* err) {
   int spins = 0;
   while (__hip_atomic_load(prog, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < c) {
     if (++spins > kSpinLimit || gave_up(err)) {
@@ -143,16 +158,6 @@ __device__ __noinline__ void wait_progress(int* prog, int c, int* err) {
     }
     __builtin_amdgcn_s_sleep(1);
   }
-}
-
-__device__ __forceinline__ float gvalue(unsigned long long v, float off) {
-  return __builtin_bit_cast(float, static_cast<uint32_t>(v)) +
-         (__builtin_bit_cast(float, static_cast<uint32_t>(v >> 32)) - off);
-}
-
-__device__ __forceinline__ float lvalue(unsigned long long v, float off) {
-  const int o = static_cast<int>(static_cast<uint32_t>(v >> 32)) >> 8;
-  return __builtin_bit_cast(float, static_cast<uint32_t>(v)) + (static_cast<float>(o) - off);
 }
 
 struct Shared {
@@ -166,9 +171,8 @@ struct Ctx {
   int b, T, U, j, k, lane;
   int64_t start;
   bool vl, sk;
-  const float* E;           // emission of this lane's label at row 0 (row stride Es)
-  const float* Eb;          // blank emission at row 0
-  int64_t Es;
+  int eidx;                 // this lane's label column in the emission table (U+1: the -1e30 column)
+  int64_t Es;               // floats per emission row
   const unsigned long long* gin;  // global ring read by this block (row-indexed)
   unsigned long long* gout;       // global ring written by this block
   unsigned long long* lin;        // LDS ring read by this block
@@ -177,7 +181,7 @@ struct Ctx {
   int* prog_cons;
   int* prog_self;
   int* sig;                 // this block's offset per chunk, at the row of the chunk's first frame
-  float* ab;                // this block's 128 states per row, at this lane's pair
+  float* ab;                // this block's 128 states per row (row 0)
   int* err;
 };
 
@@ -189,118 +193,143 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
   const int edge = BETA ? 0 : 63;
   const int64_t drow = BETA ? -1 : 1;
   const int64_t r0 = cx.start + (BETA ? T - 1 : 0);  // row of step 0
-  const bool vl = cx.vl, sk = cx.sk;
-  const bool vb = k <= U;
+  const bool sk = cx.sk;
+  const int64_t Es = cx.Es;
   int* err = cx.err;
 
   auto dpp = [&](float old, float x) { return BETA ? dpp_f32<0x130>(old, x) : dpp_f32<0x138>(old, x); };
-  auto row = [&](int step) { return r0 + drow * step; };
-  // lane-distributed loads of chunk c (steps 1 + c*kK ...): lane i holds the blank emission of its
-  // frame and, across a segment boundary, the neighbour slot of the frame before; clamped to the
-  // utterance
-  auto lane_loads = [&](int c, float& eb, unsigned long long& hg) {
-    eb = cx.Eb[row(min(1 + c * kK + lane, T - 1)) * cx.Es];
-    if (IN_GLOBAL) hg = gload(cx.gin + row(min(c * kK + lane, T - 1)));
-  };
+  auto row = [&](int64_t step) { return r0 + drow * step; };
+  // lowest row of chunk c (its first frame for alpha, its last for beta) and a frame's place in it
+  auto chunk_lo = [&](int c) { return BETA ? row((int64_t)(c + 1) * kK) : row(1 + (int64_t)c * kK); };
+  auto in_chunk = [&](int i) { return BETA ? kK - 1 - i : i; };
 
   // ---- first frame ----
   float xb, xl, off = 0.0f;
   {
     const int64_t r = row(0);
-    const float eb = cx.Eb[r * cx.Es];
-    const float el = cx.E[r * cx.Es];
+    const float eb = P.E[r * Es];
+    const float el = P.E[r * Es + cx.eidx];
     const bool first = BETA ? (k == U) : (k == 0);
     xb = first ? eb : kNeg;
-    xl = (first && vl) ? el : kNeg;
-    *reinterpret_cast<float2*>(cx.ab + r * 128) = BETA ? make_float2(xl, xb) : make_float2(xb, xl);
-    const float e = lanef(xl, edge);
-    if (OUT_GLOBAL) gstore(cx.gout + r, pack_global(e, 0.0f));
-    else lstore(cx.lout + 0, pack_lds(e, 0.0f, 0));
-  }
-
-  // build a lead over the producer: two chunks across a segment boundary (its slots are prefetched
-  // a chunk ahead), a few frames inside a segment (the LDS slot is read one frame ahead)
-  if (IN_GLOBAL && T > 1) wait_global(cx.gin + row(min(2 * kK, T - 1)), err);
-  if (!IN_GLOBAL && T > 1) {
-    const int s0 = min(4, T - 1);
-    wait_lds(cx.lin + (s0 & (kR - 1)), s0, err);
-  }
-
-  // label emissions: register i holds the frame of step 1 + c*kK + i of the current chunk c and is
-  // reloaded with the frame one chunk later right after its use (may read into the row padding)
-  float el[kK];
-  {
-    const float* e = cx.E + row(1) * cx.Es;
-#pragma unroll
-    for (int i = 0; i < kK; ++i) el[i] = e[drow * i * cx.Es];
-  }
-  float eb = 0.0f, ebn = 0.0f;
-  unsigned long long hg = 0, hgn = 0;
-  lane_loads(0, eb, hg);
-  bool more = T > 1;
-  unsigned long long lnext = 0;  // LDS input: the slot of the previous frame, read one frame ahead
-  if (!IN_GLOBAL) lnext = lload(cx.lin);
-  float* abp = cx.ab + row(1) * 128;
-
-  auto run_chunk = [&](int c) {
-    lane_loads(c + 1, ebn, hgn);
-    if (!OUT_GLOBAL && cx.lout_live && c >= 1) wait_progress(cx.prog_cons, c - 1, err);
-    cx.sig[row(min(1 + c * kK, T - 1))] = static_cast<int>(off);  // this chunk's offset
-    const float* enext = cx.E + row(1 + (c + 1) * kK) * cx.Es;
-#pragma unroll
-    for (int i = 0; i < kK; ++i) {
-      const int step = 1 + c * kK + i;
-      if (step >= T) {
-        more = false;
-        break;
-      }
-      float h;
-      if (IN_GLOBAL) {
-        unsigned long long v = lane64(hg, i);
-        if (v == kEmpty) v = wait_global(cx.gin + row(step - 1), err);
-        h = gvalue(v, off);
-      } else {
-        unsigned long long v = uniform64(lnext);
-        if (((v >> 32) & 0xffu) != lds_tag(step - 1)) v = wait_lds(cx.lin + ((step - 1) & (kR - 1)), step - 1, err);
-        h = lvalue(v, off);
-        lnext = lload(cx.lin + (step & (kR - 1)));
-      }
-      const float n = dpp(h, xl);
-      const float nb = lse2(xb, n) + lanef(eb, i);
-      const float nl = lse3(xl, xb, sk ? n : kNeg) + el[i];
-      el[i] = enext[drow * i * cx.Es];
-      xb = vb ? nb : kNeg;
-      xl = vl ? nl : kNeg;
-      *reinterpret_cast<float2*>(abp) = BETA ? make_float2(xl, xb) : make_float2(xb, xl);
-      abp += drow * 128;
-      const float e = lanef(xl, edge);
-      if (OUT_GLOBAL) gstore(cx.gout + row(step), pack_global(e, off));
-      else lstore(cx.lout + (step & (kR - 1)), pack_lds(e, off, step));
+    xl = (first && cx.vl) ? el : kNeg;
+    *reinterpret_cast<float2*>(cx.ab + r * 128 + 2 * lane) = BETA ? make_float2(xl, xb) : make_float2(xb, xl);
+    if (lane == edge) {
+      const unsigned long long v = pack(xl, slot_hi(0.0f, -1));
+      if (OUT_GLOBAL) gstore(cx.gout + r, v);
+      else lstore(cx.lout + (kR - 1), v);
     }
-    if (!IN_GLOBAL && lane == 0) __hip_atomic_store(cx.prog_self, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    // shift by the block's integer maximum so the values stay near 0
-    const float mx = wave_max(fmaxf(xb, xl));
-    const float d = mx > kNegHalf ? floorf(mx) : 0.0f;
-    xb -= d;
-    xl -= d;
-    off += d;
-    eb = ebn;
-    hg = hgn;
-  };
+  }
 
-  // the first chunk is peeled so that the loop starts from the same memory-counter state it
-  // leaves with, and the compiler's waits do not drain the stores and loads in flight
-  int c = 0;
-  if (more) run_chunk(c++);
-  while (more) run_chunk(c++);
+  const int nsteps = T - 1;
+  if (nsteps > 0) {
+    // build a lead over a producer in another segment: its slots are loaded a chunk ahead
+    if (IN_GLOBAL) {
+      const unsigned long long* p = cx.gin + row(min(2 * kK, T - 1));
+      wait_global(p, gload(p), true, err);
+    }
+    // label emissions of chunk 0 (register i: the frame of step 1 + i); blank emissions and, across
+    // a segment boundary, the neighbour slots of chunk 0, one per lane
+    float el[kK];
+    {
+      const __amdgpu_buffer_rsrc_t er = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(P.E + chunk_lo(0) * Es), 0, static_cast<int>(kK * Es * 4), kRsrcWord3);
+#pragma unroll
+      for (int i = 0; i < kK; ++i)
+        el[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(er, cx.eidx * 4, in_chunk(i) * Es * 4, 0));
+    }
+    const int l16 = lane & (kK - 1);
+    float ebv = P.E[row(1 + l16) * Es];
+    unsigned long long hraw = 0;
+    if (IN_GLOBAL) hraw = gload(cx.gin + row(min(l16, nsteps)));
+
+    auto run_chunk = [&](auto full, int c, int nvalid) {
+      constexpr bool FULL = decltype(full)::value;
+      // neighbour values of this chunk: lane i < kK holds the producer's frame at step c*kK + i
+      const bool need = lane < (FULL ? kK : nvalid);
+      const int want = lane == 0 ? c - 1 : c;
+      const unsigned long long* lp = cx.lin + ((c * kK + l16 - 1) & (kR - 1));
+      unsigned long long raw = IN_GLOBAL ? hraw : lload(lp);
+      const bool check_cons = !OUT_GLOBAL && cx.lout_live && c >= kR / kK - 1;
+      const int cons = check_cons ? __hip_atomic_load(cx.prog_cons, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0;
+      const float ebn = P.E[row(1 + (int64_t)(c + 1) * kK + l16) * Es];
+      cx.sig[row(1 + (int64_t)c * kK)] = static_cast<int>(off);
+      if (IN_GLOBAL) {
+        if (__ballot(need && !global_ok(raw))) raw = wait_global(cx.gin + row(min(c * kK + l16, nsteps)), raw, need, err);
+        hraw = gload(cx.gin + row(min((c + 1) * kK + l16, nsteps)));
+      } else {
+        if (__ballot(need && !lds_ok(raw, want))) raw = wait_lds(lp, raw, need, want, err);
+        if (lane == 0) __hip_atomic_store(cx.prog_self, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      // the consumer of this block's LDS ring must have taken the chunk whose slots this one reuses
+      if (check_cons && cons < c - (kR / kK - 1)) wait_progress(cx.prog_cons, c - (kR / kK - 1), err);
+      const float hv = slot_value(raw, off);
+      const __amdgpu_buffer_rsrc_t ab = __builtin_amdgcn_make_buffer_rsrc(cx.ab + chunk_lo(c) * 128, 0, kK * 512,
+                                                                          kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t er = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(P.E + chunk_lo(c + 1) * Es), 0, static_cast<int>(kK * Es * 4), kRsrcWord3);
+      const uint32_t hi = slot_hi(off, c);
+      unsigned long long* gslot = cx.gout + row(1 + (int64_t)c * kK);
+      unsigned long long* lslot = cx.lout + ((c * kK) & (kR - 1));
+      // the neighbour of frame 0; each later frame's neighbour is formed as soon as the label value
+      // it shifts exists, ahead of that frame's stores
+      float n = dpp(lanef(hv, 0), xl);
+#pragma unroll
+      for (int i = 0; i < kK; ++i) {
+        if (!FULL && i >= nvalid) continue;  // uniform: the last chunk's missing frames
+        // blank: lse(blank, neighbour) + emission; label: lse(label, skip ? that sum : blank) + emission
+        const float d1 = xb - n;
+        const float l1 = log2_fast(1.0f + exp2_fast(-fabsf(d1)));
+        const float h1 = __builtin_amdgcn_fmed3f(xb, n, 3.0e38f);
+        const float t = h1 + l1;
+        const float nb = (h1 + lanef(ebv, i)) + l1;
+        const float a2 = sk ? t : xb;
+        const float d2 = xl - a2;
+        const float l2 = log2_fast(1.0f + exp2_fast(-fabsf(d2)));
+        const float h2 = __builtin_amdgcn_fmed3f(xl, a2, 3.0e38f);
+        const float nl = (h2 + el[i]) + l2;
+        if (i + 1 < kK) n = dpp(lanef(hv, i + 1), nl);
+        el[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(er, cx.eidx * 4, in_chunk(i) * Es * 4, 0));
+        xb = nb;
+        xl = nl;
+        const u32x2 st = BETA ? u32x2{__builtin_bit_cast(uint32_t, xl), __builtin_bit_cast(uint32_t, xb)}
+                              : u32x2{__builtin_bit_cast(uint32_t, xb), __builtin_bit_cast(uint32_t, xl)};
+        __builtin_amdgcn_raw_buffer_store_b64(st, ab, lane * 8, in_chunk(i) * 512, 0);
+        if (lane == edge) {
+          const unsigned long long v = pack(xl, hi);
+          if (OUT_GLOBAL) gstore(gslot + drow * i, v);
+          else lstore(lslot + i, v);
+        }
+      }
+      // shift by the block's integer maximum so the values stay near 0
+      const float mx = wave_max(fmaxf(xb, xl));
+      const float d = mx > kNegHalf ? floorf(mx) : 0.0f;
+      xb -= d;
+      xl -= d;
+      off += d;
+      ebv = ebn;
+    };
+
+    // the first chunk is peeled so that the loop starts from the same memory-counter state it
+    // leaves with, and the compiler's waits do not drain the stores and loads in flight
+    const int nfull = nsteps / kK, nrem = nsteps % kK;
+    if (nfull > 0) run_chunk(std::true_type{}, 0, kK);
+    for (int c = 1; c < nfull; ++c) run_chunk(std::true_type{}, c, kK);
+    if (nrem > 0) run_chunk(std::false_type{}, nfull, nrem);
+  }
 
   // ---- likelihood: the block holding the last states (alpha) or the first states (beta) ----
   const bool owner = BETA ? (cx.j == 0) : (cx.j == (U >> 6));
   if (!owner) return;
   float h = kNeg;
-  if (!BETA) {
-    if (IN_GLOBAL) h = gvalue(wait_global(cx.gin + row(T - 1), err), off);
-    else h = lvalue(wait_lds(cx.lin + ((T - 1) & (kR - 1)), T - 1, err), off);
+  if (!BETA) {  // the producer's label at the last frame
+    const int step = T - 1;
+    if (IN_GLOBAL) {
+      const unsigned long long* p = cx.gin + row(step);
+      h = slot_value(wait_global(p, gload(p), true, err), off);
+    } else {
+      const unsigned long long* p = cx.lin + ((step - 1) & (kR - 1));
+      h = slot_value(wait_lds(p, lload(p), true, chunk_of(step), err), off);
+    }
   }
   // alpha: blank of pair U with the label of pair U-1; beta: blank of pair 0 with the label of pair 1
   const float n = dpp(h, xl);
@@ -344,10 +373,8 @@ __device__ __forceinline__ void run_wave(const Layout& L, const Pointers& P, Sha
   cx.vl = beta ? (k >= 1 && k <= U) : (k < U);
   if (!beta) cx.sk = cx.vl && k >= 1 && lab[k + 1] != lab[k];     // skip 2k-1 -> 2k+1
   else cx.sk = cx.vl && k + 1 <= U && lab[k] != lab[k + 1];       // skip 2k-1 -> 2k+1 (backwards)
-  const int eidx = cx.vl ? (beta ? k : k + 1) : 0;
+  cx.eidx = cx.vl ? (beta ? k : k + 1) : U + 1;
   cx.Es = L.E_stride;
-  cx.E = P.E + eidx;
-  cx.Eb = P.E;
   // neighbours: alpha takes from block j-1 and gives to j+1; beta the other way round
   const bool has_in = beta ? (j + 1 < G) : (j > 0);
   const bool has_out = beta ? (j > 0) : (j + 1 < G);
@@ -364,7 +391,7 @@ __device__ __forceinline__ void run_wave(const Layout& L, const Pointers& P, Sha
   cx.prog_cons = &sh.prog[beta ? max(w - 1, 0) : min(w + 1, kWaves - 1)];
   cx.prog_self = &sh.prog[w];
   cx.sig = P.sig + (dir * Gm + j) * TT;
-  cx.ab = P.AB + (dir * Gm + j) * TT * 128 + 2 * lane;
+  cx.ab = P.AB + (dir * Gm + j) * TT * 128;
   cx.err = &P.ctl->err;
   if (!beta) {
     if (in_global) {
@@ -387,7 +414,9 @@ __device__ __forceinline__ void run_wave(const Layout& L, const Pointers& P, Sha
 
 __global__ void __launch_bounds__(256, 1) chain_workers(Layout L, Pointers P) {
   __shared__ Shared sh;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index and the claimed item are wave-uniform: say so, so that every address derived
+  // from them stays in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qlen = P.ctl->qlen;
   for (;;) {
     // a fresh segment: clear the rings (tag 0 matches no frame) and the progress words
@@ -395,9 +424,9 @@ __global__ void __launch_bounds__(256, 1) chain_workers(Layout L, Pointers P) {
     if (tid < kWaves) sh.prog[tid] = -1;
     if (tid == 0) sh.item = atomicAdd(&P.ctl->qcount, 1);
     __syncthreads();
-    const int idx = sh.item;
+    const int idx = __builtin_amdgcn_readfirstlane(sh.item);
     if (idx >= qlen) break;
-    const int item = P.items[idx];
+    const int item = __builtin_amdgcn_readfirstlane(P.items[idx]);
     run_wave(L, P, sh, item >> 12, item & 4095, w, lane);
     __syncthreads();
   }

@@ -45,10 +45,11 @@ constexpr int kEPad = 40;
 
 struct Layout {
   int64_t T_total, D, B, Umax;
-  int64_t E_stride;  // floats per row of the emission table (>= Umax + 1)
+  int64_t E_stride;  // floats per row of the emission table (>= Umax + 2)
   int64_t Gmax;      // state-pair blocks of the longest target: ceil((Umax + 1) / 64)
   int64_t Dw;        // 32-bit words of a class bitmap: ceil(D / 32)
-  size_t off_cbits, off_cpref, off_dmap, off_meta, off_lab, off_rowmap, off_rowoff, off_E, off_AB, off_nll, off_llb, off_lsh, off_w, off_ring, off_nring,
+  int64_t C_stride;  // floats per row of the compact class sums (>= Umax + 1)
+  size_t off_cbits, off_cpref, off_dmap, off_meta, off_lab, off_rowmap, off_rowoff, off_E, off_AB, off_nll, off_llb, off_lsh, off_w, off_post, off_ring, off_nring,
       off_sig, off_items, off_ctl, total;
 };
 
@@ -67,7 +68,7 @@ struct Pointers {
   int* lab;      // (B, Umax + 1): j = 0 the blank, j >= 1 targets[b][j-1]
   int* rowmap;   // (T_total,): owning utterance or -1
   int* rowoff;   // (T_total,): integer offset subtracted from the row's gathered log2 emissions
-  float* E;      // (T_total, E_stride), kEPad rows of padding on either side
+  float* E;      // (T_total, E_stride): columns 0..U the labels, U+1 holds -1e30; kEPad rows of padding on either side
   // (2, Gmax, T_total, 128): normalised log2 alpha (direction 0) and beta (direction 1) per block
   // of 64 state pairs and per row.  Alpha pair k sits at 2k, 2k+1 (states 2k, 2k+1); beta pair k at
   // 2k, 2k+1 (states 2k-1, 2k), i.e. beta of state s at position s+1, all relative to the block.
@@ -77,7 +78,7 @@ struct Pointers {
   double* lsh;   // (B,) log2 likelihood from the alpha side without the row offsets
   float* w;      // (B,) gradient weight
   unsigned long long* ring;  // (2, Gmax, T_total) block-boundary values (value, offset) per frame
-  unsigned long long* nring; // (T_total,) (-inf, 0) in every slot: the neighbour of an edge block
+  unsigned long long* nring; // (T_total,) a written (-inf, offset 0) slot everywhere: the neighbour of an edge block
   int* sig;      // (2, Gmax, T_total) integer offset of each block's stored values, per chunk
   int* items;    // (2 B Gmax) queued recursion blocks: (utterance * 2 + direction) << 12 | block
   ChainCtl* ctl;
@@ -85,6 +86,7 @@ struct Pointers {
   uint32_t* cbits;  // (B, Dw) bitmap of the classes present
   int* cpref;       // (B, Dw) number of classes present in the words before each word
   int* dmap;        // (B, Umax + 1) rank among the present classes of lab[j]
+  float* post;      // (T_total, C_stride) per row: the class sums times w / z, by class rank
 };
 
 Pointers carve(void* workspace, const Layout& L);
@@ -306,6 +308,7 @@ hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, h
 hipError_t launch_weights(const Inputs& in, const Layout& L, const Pointers& P, float* losses_out, float* reduced_out,
                           hipStream_t s);
 hipError_t launch_classes(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
+hipError_t launch_posteriors(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
 hipError_t launch_dense(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 hipError_t launch_zero_bytes(void* p, int64_t nbytes, hipStream_t s);

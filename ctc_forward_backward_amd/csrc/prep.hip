@@ -72,53 +72,77 @@ __global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers
   for (int t = threadIdx.x; t < mm.T; t += blockDim.x) P.rowmap[mm.start + t] = b;
 }
 
-// One wave per owned row: the log2 emissions of the row at the utterance's U+1 distinct classes,
-// minus the row's integer offset floor(max), so that the recursions work on values near 0.
-// The row is staged through LDS in tiles with aligned 16-byte loads (the label columns are
-// scattered over the row, and reading them one by one would fetch a whole sector each).
-constexpr int kGTile = 4096;  // elements of a row per LDS tile (one tile per wave)
+// One wave per owned row: the log2 emissions of the row at the utterance's U+1 label columns,
+// minus the row's integer offset floor(max over those columns), so that the recursions work on
+// values near 0.  Lanes read their labels' values straight from the row, so only the memory
+// sectors that hold a label are fetched (the offset needs nothing else of the row).  A wave takes
+// a contiguous range of rows: the label ids of its utterance stay in registers from row to row,
+// and for U+1 <= 512 the values too, so the table row is written once.
+constexpr int kGLab = 8;  // label columns per lane held in registers
 
 template <int DT>
-__global__ void __launch_bounds__(256) gather_kernel(Inputs in, Layout L, Pointers P) {
-  extern __shared__ float gsm[];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float* tile = gsm + wave * (kGTile + 8);
+__device__ __forceinline__ float ld1(const void* p, int64_t i) {
+  if constexpr (DT == kF32) return static_cast<const float*>(p)[i];
+  else if constexpr (DT == kF16) return static_cast<float>(static_cast<const _Float16*>(p)[i]);
+  else return __builtin_bit_cast(float, static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+}
+
+template <int DT>
+__global__ void __launch_bounds__(256) gather_kernel(Inputs in, Layout L, Pointers P, int rows_per_wave) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t r0 = wid * rows_per_wave, r1 = min(r0 + rows_per_wave, L.T_total);
   const int64_t D = L.D;
-  for (int64_t r = (int64_t)blockIdx.x * 4 + wave; r < L.T_total; r += (int64_t)gridDim.x * 4) {
-    const int b = P.rowmap[r];
+  int cur_b = -1, U = 0;
+  const int* lab = nullptr;
+  int col[kGLab];
+  for (int64_t r = r0; r < r1; ++r) {
+    const int b = __builtin_amdgcn_readfirstlane(P.rowmap[r]);
     if (b < 0) continue;
-    const int U = P.meta[b].U;
-    const int* lab = P.lab + (int64_t)b * (L.Umax + 1);
+    if (b != cur_b) {
+      U = P.meta[b].U;
+      lab = P.lab + (int64_t)b * (L.Umax + 1);
+#pragma unroll
+      for (int k = 0; k < kGLab; ++k) col[k] = lab[min(lane + 64 * k, U)];
+      cur_b = b;
+    }
     float* E = P.E + r * L.E_stride;
+    const int64_t row = r * D;
     float mx = kNeg;
     int nan = 0;
-    for (int64_t t0 = 0; t0 < D; t0 += kGTile) {
-      const int64_t f0 = r * D + t0, f1 = f0 + min((int64_t)kGTile, D - t0);
-      const int64_t base = f0 & ~int64_t(7);  // tile[f - base] holds element f; chunks land 8-aligned
-      wave_segment<DT>(
-          in.log_probs, f0, f1, lane,
-          [&](int64_t, int64_t f, const float* v) {
-            float4* t = reinterpret_cast<float4*>(tile + (f - base));
-            t[0] = make_float4(v[0], v[1], v[2], v[3]);
-            t[1] = make_float4(v[4], v[5], v[6], v[7]);
-          },
-          [&](int64_t f) { tile[f - base] = load_lp(in.log_probs, DT, f); });
-      // the tile was written by this wave's lanes; LDS operations of one wave complete in order
-      for (int j = lane; j <= U; j += 64) {
-        const int64_t c = lab[j];
-        if (c >= t0 && c < t0 + kGTile) {
-          float v = tile[r * D + c - base] * kLog2e;
-          nan |= (v != v);
-          v = fmaxf(v, kNeg);  // -inf (and NaN, flagged above) become the finite sentinel
-          mx = fmaxf(mx, v);
-          E[j] = v;
-        }
+    if (U < 64 * kGLab) {
+      float v[kGLab];
+#pragma unroll
+      for (int k = 0; k < kGLab; ++k) v[k] = ld1<DT>(in.log_probs, row + col[k]);  // all loads in flight
+#pragma unroll
+      for (int k = 0; k < kGLab; ++k) {
+        const bool ok = lane + 64 * k <= U;
+        float x = v[k] * kLog2e;
+        nan |= ok && (x != x);
+        x = fmaxf(x, kNeg);  // -inf (and NaN, flagged above) become the finite sentinel
+        v[k] = x;
+        if (ok) mx = fmaxf(mx, x);
       }
+      mx = wave_max(mx);
+      const float off = mx > kNegHalf ? floorf(mx) : 0.0f;
+#pragma unroll
+      for (int k = 0; k < kGLab; ++k)
+        if (lane + 64 * k <= U) E[lane + 64 * k] = v[k] - off;
+      if (lane == 0) P.rowoff[r] = static_cast<int>(off);
+    } else {  // long targets: two passes over the table row
+      for (int j = lane; j <= U; j += 64) {
+        float x = ld1<DT>(in.log_probs, row + lab[j]) * kLog2e;
+        nan |= (x != x);
+        x = fmaxf(x, kNeg);
+        mx = fmaxf(mx, x);
+        E[j] = x;
+      }
+      mx = wave_max(mx);
+      const float off = mx > kNegHalf ? floorf(mx) : 0.0f;
+      for (int j = lane; j <= U; j += 64) E[j] -= off;
+      if (lane == 0) P.rowoff[r] = static_cast<int>(off);
     }
-    mx = wave_max(mx);
-    const float off = mx > kNegHalf ? floorf(mx) : 0.0f;
-    for (int j = lane; j <= U; j += 64) E[j] -= off;
-    if (lane == 0) P.rowoff[r] = static_cast<int>(off);
+    if (lane == 0) E[U + 1] = kNeg;  // the column of label states that do not exist
     if (nan) atomicOr(&P.meta[b].flags, 1);
   }
 }
@@ -304,19 +328,16 @@ hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, h
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  const int64_t want = (L.T_total + 3) / 4;
-  const int grid = static_cast<int>(want < 2 * (int64_t)cus ? want : 2 * (int64_t)cus);
-  const size_t lds = 4 * (kGTile + 8) * sizeof(float);
-  auto launch = [&](auto kernel) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (err != hipSuccess) return err;
-    kernel<<<grid, 256, lds, s>>>(in, L, P);
-    return hipGetLastError();
-  };
-  if (in.dtype == kF32) return launch(&gather_kernel<kF32>);
-  if (in.dtype == kF16) return launch(&gather_kernel<kF16>);
-  return launch(&gather_kernel<kBF16>);
+  // about 32 waves per compute unit, each on a contiguous range of rows
+  const int64_t waves = 32 * (int64_t)(cus > 0 ? cus : 256);
+  const int64_t rpw = (L.T_total + waves - 1) / waves;
+  const int64_t wanted_waves = (L.T_total + rpw - 1) / rpw;
+  const int grid = static_cast<int>((wanted_waves + 3) / 4);
+  const int rows = static_cast<int>(rpw);
+  if (in.dtype == kF32) gather_kernel<kF32><<<grid, 256, 0, s>>>(in, L, P, rows);
+  else if (in.dtype == kF16) gather_kernel<kF16><<<grid, 256, 0, s>>>(in, L, P, rows);
+  else gather_kernel<kBF16><<<grid, 256, 0, s>>>(in, L, P, rows);
+  return hipGetLastError();
 }
 
 hipError_t launch_classes(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {
@@ -335,11 +356,12 @@ hipError_t launch_classes(const Inputs& in, const Layout& L, const Pointers& P, 
 hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {
   (void)in;
   if (L.B == 0) return hipGetLastError();
-  // every ring slot starts empty (all ones); a block publishes (value, offset) into it once
+  // every ring slot starts unwritten (zero: the written mark 0x80 of its high word is clear); a
+  // block publishes (value, offset << 8 | 0x80 | tag) into it once
   const int64_t words = 2 * 2 * L.Gmax * L.T_total;
-  if (words > 0) fill_i32_kernel<<<grid_for(words, 256), 256, 0, s>>>(reinterpret_cast<int*>(P.ring), words, -1);
-  // the neighbour of an edge block: (-inf, offset 0) in every slot
-  const unsigned long long none = (unsigned long long)__builtin_bit_cast(uint32_t, kNeg);
+  if (words > 0) fill_i32_kernel<<<grid_for(words, 256), 256, 0, s>>>(reinterpret_cast<int*>(P.ring), words, 0);
+  // the neighbour of an edge block: (-inf, offset 0, written) in every slot
+  const unsigned long long none = (unsigned long long)__builtin_bit_cast(uint32_t, kNeg) | (0x80ull << 32);
   if (L.T_total > 0) fill_u64_kernel<<<grid_for(L.T_total, 256), 256, 0, s>>>(P.nring, L.T_total, none);
   const int sort = L.B <= 8192 ? 1 : 0;
   const size_t lds = sort ? 2 * sizeof(int) * (size_t)L.B : 0;

@@ -1,0 +1,241 @@
+// Per-row work of the packed CTC gradient: the posteriors of one row (class sums) and the gradient
+// row itself.  Device functions only: the standalone row kernels and the persistent worker that
+// overlaps them with the recursions both call these.
+//
+// Method: NVIDIA-NeMo/Speech pull request "feat(asr): native CTC loss kernel over sequence-packed log
+// probabilities", Triton file, `_beta_grad_kernel` and `_PackedCTCLoss.backward`: the posterior of
+// state s at frame t is exp(alpha + beta - lp + nll) scaled by the utterance's gradient weight and
+// formed only when that weight is non-zero; each gradient row is weight * exp(lp) minus the
+// posteriors summed per class (blank states at the blank column, label states at their label's
+// column); rows owned by no utterance are zero; the row is stored in the dtype of the log probs.
+//
+// Design for gfx950:
+//   - posterior_row: one pass over the stored alpha and beta, 2^(alpha + beta - lp) taken relative
+//     to the likelihood the alpha recursion reached (the block offsets of alpha and beta meet in
+//     that constant, so every term is at most about 1).  Blank states are summed in registers,
+//     label states added into an LDS array indexed by the rank of their class among the
+//     utterance's classes (at most U+1 entries).  The frame's own total z of the terms normalises
+//     them, so the posteriors of every frame sum to exactly the weight (the page's
+//     exp(alpha + beta - lp + nll) for a feasible utterance, with the rounding drift of the
+//     recursions divided out).  The row's class sums, times w / z, are written compactly: U+1
+//     floats per row.
+//   - dense_row: the whole row (up to 16 aligned 16-byte chunks per lane) and its compact class
+//     sums are loaded together; the row is streamed once, and a per-utterance class bitmap with
+//     per-word prefix counts (in LDS) tells which columns of a chunk carry a class and its rank,
+//     so the correction is applied in registers before the single store.
+#pragma once
+
+#include "pctc_internal.h"
+
+namespace pctc {
+namespace rows {
+
+constexpr int kBlocks = 4;  // state-pair blocks whose loads are issued together
+constexpr int kLook = 4;    // row chunks whose class lookups are issued together
+constexpr int kPost = 8;    // compact class sums per lane held in registers (U+1 <= 512)
+
+// aligned 8-element row chunks per lane loaded at once (the whole row for D <= 8192 at 2 bytes)
+template <int DT>
+constexpr int row_batch() { return DT == kF32 ? 8 : 16; }
+
+// a row gets a gradient from its utterance only if the utterance has a non-zero weight and an
+// alignment (a NaN input makes the loss NaN, which also fails the test)
+__device__ __forceinline__ bool row_live(const Pointers& P, int b, float& w) {
+  w = b >= 0 ? P.w[b] : 0.0f;
+  return w != 0.0f && b >= 0 && P.nll[b] < (double)INFINITY;
+}
+
+// class sums of row r of live utterance b (weight w) into P.post; acc: this wave's LDS (C_stride)
+__device__ __forceinline__ void posterior_row(const Layout& L, const Pointers& P, float* acc, int64_t r, int b,
+                                              float w, int lane) {
+  const int64_t TT = L.T_total, Gm = L.Gmax;
+  const Meta m = P.meta[b];
+  const int U = m.U, G = (U + 64) >> 6;
+  const int64_t start = m.start, T = m.T;
+  // each recursion block stores its offset once per chunk, at the row of the chunk's first frame
+  const int64_t sa = r - start, sb = start + T - 1 - r;
+  const int64_t rowa = sa == 0 ? -1 : start + 1 + ((sa - 1) / kChunk) * kChunk;
+  const int64_t rowb = sb == 0 ? -1 : start + T - 1 - (1 + ((sb - 1) / kChunk) * kChunk);
+  auto offA = [&](int j) { return rowa < 0 ? 0 : P.sig[j * TT + rowa]; };
+  auto offB = [&](int j) { return rowb < 0 ? 0 : P.sig[(Gm + j) * TT + rowb]; };
+  const double lsh = P.lsh[b];
+  const float* Er = P.E + r * L.E_stride;
+  const float eb = Er[0];
+  const int* dmap = P.dmap + (int64_t)b * (L.Umax + 1);
+  // LDS operations of one wave complete in order: zeroing, atomics and reads need no barrier
+  for (int i = lane; i <= U; i += 64) acc[i] = 0.0f;
+
+  float z = 0.0f, bsum = 0.0f;
+  for (int j0 = 0; j0 < G; j0 += kBlocks) {
+    // pair k = 64 j + lane: state 2k (blank) takes alpha at 2k and beta at 2k + 1; state 2k + 1
+    // (label k + 1) alpha at 2k + 1 and beta at 2k + 2, which for lane 63 is the next block's first
+    float2 a[kBlocks];
+    float b0[kBlocks], b1[kBlocks], el[kBlocks], c0[kBlocks], c1[kBlocks];
+    int d1[kBlocks];
+#pragma unroll
+    for (int u = 0; u < kBlocks; ++u) {
+      const int j = j0 + u, k = 64 * j + lane;
+      a[u] = make_float2(kNeg, kNeg);
+      b0[u] = b1[u] = el[u] = 0.0f;
+      c0[u] = c1[u] = 0.0f;
+      d1[u] = 0;
+      if (j < G) {
+        const int oa = offA(j), ob0 = offB(j);
+        const int ob1 = lane < 63 ? ob0 : (j + 1 < G ? offB(j + 1) : ob0);
+        c0[u] = static_cast<float>((double)(oa + ob0) - lsh);
+        c1[u] = static_cast<float>((double)(oa + ob1) - lsh);
+        const int64_t rb = ((Gm + j) * TT + r) * 128;
+        if (k <= U) {
+          a[u] = *reinterpret_cast<const float2*>(P.AB + ((int64_t)j * TT + r) * 128 + 2 * lane);
+          b0[u] = P.AB[rb + 2 * lane + 1];
+        }
+        if (k < U) {  // then for lane 63 the next block exists
+          b1[u] = P.AB[lane < 63 ? rb + 2 * lane + 2 : rb + TT * 128];
+          el[u] = Er[k + 1];
+          d1[u] = dmap[k + 1];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBlocks; ++u) {
+      const int k = 64 * (j0 + u) + lane;
+      // each term is at most about 1; the clamp only guards the exponent against garbage
+      const float p0 = k <= U ? exp2_fast(fminf(a[u].x + b0[u] - eb + c0[u], 64.0f)) : 0.0f;
+      const float p1 = k < U ? exp2_fast(fminf(a[u].y + b1[u] - el[u] + c1[u], 64.0f)) : 0.0f;
+      z += p0 + p1;
+      bsum += p0;
+      if (k < U) atomicAdd(&acc[d1[u]], p1);
+    }
+  }
+  z = wave_sum(z);
+  bsum = wave_sum(bsum);
+  if (lane == 0) atomicAdd(&acc[dmap[0]], bsum);
+  const float scale = z > 0.0f ? w / z : 0.0f;
+  float* out = P.post + r * L.C_stride;
+  for (int i = lane; i <= U; i += 64) out[i] = acc[i] * scale;
+}
+
+// row r of a dead utterance (zero weight: 0, no alignment or NaN: NaN) or of no utterance (0)
+template <int DT>
+__device__ __forceinline__ void fill_row(const Layout& L, void* grad, int64_t r, float fill, int lane) {
+  const int64_t f0 = r * L.D, f1 = f0 + L.D;
+  wave_segment<DT>(
+      nullptr, f0, f1, lane,
+      [&](int64_t q, int64_t, const float*) {
+        const float v[8] = {fill, fill, fill, fill, fill, fill, fill, fill};
+        store8<DT>(grad, q, v);
+      },
+      [&](int64_t f) { store_grad(grad, DT, f, fill); });
+}
+
+// gradient row r of live utterance b (weight w), its class sums taken from P.post.  lds: this
+// wave's words, the class sums (C_stride) then the class bitmap (Dw) and its prefix counts (Dw);
+// cur_b: the utterance whose bitmap the LDS holds (updated here).
+template <int DT>
+__device__ __forceinline__ void dense_row(const Inputs& in, const Layout& L, const Pointers& P, void* grad,
+                                          uint32_t* lds, int64_t r, int b, float w, int lane, int& cur_b) {
+  const int Dw = static_cast<int>(L.Dw);
+  float* acc = reinterpret_cast<float*>(lds);
+  uint32_t* bits = lds + L.C_stride;
+  const int* pref = reinterpret_cast<const int*>(bits + Dw);
+  const int64_t D = L.D;
+  constexpr int RB = row_batch<DT>();
+  const int64_t f0 = r * D, f1 = f0 + D;
+  // aligned chunks [qb, qe) of the row: the first batch and the row's class sums load together
+  int64_t a0 = (f0 + 7) & ~int64_t(7), a1 = f1 & ~int64_t(7);
+  if (a0 > a1) a0 = a1 = f1;  // shorter than one aligned chunk: all single elements
+  const int64_t qb = a0 >> 3, qe = a1 >> 3;
+  Raw8<DT> raw[RB];
+  if (qe > qb) {
+#pragma unroll
+    for (int u = 0; u < RB; ++u) raw[u] = ld8<DT>(in.log_probs, min(qb + lane + 64 * u, qe - 1));  // clamped
+  }
+  const int U = P.meta[b].U;
+  const float* pr = P.post + r * L.C_stride;
+  float pv[kPost];
+#pragma unroll
+  for (int k = 0; k < kPost; ++k) pv[k] = pr[min(lane + 64 * k, U)];
+  if (b != cur_b) {  // this utterance's class bitmap and prefix counts into the wave's LDS
+    const uint32_t* gb = P.cbits + (int64_t)b * Dw;
+    const int* gp = P.cpref + (int64_t)b * Dw;
+    for (int i = lane; i < Dw; i += 64) {
+      bits[i] = gb[i];
+      bits[Dw + i] = static_cast<uint32_t>(gp[i]);
+    }
+    cur_b = b;
+  }
+  // LDS operations of one wave complete in order: these writes precede every read below
+#pragma unroll
+  for (int k = 0; k < kPost; ++k)
+    if (lane + 64 * k <= U) acc[lane + 64 * k] = pv[k];
+  for (int i = lane + 64 * kPost; i <= U; i += 64) acc[i] = pr[i];  // long targets
+
+  // stream the row once: w * exp(lp) minus the class posterior at the columns that carry one.
+  // The classes of an aligned chunk of 8 columns are consecutive in rank order, so one rank per
+  // chunk (classes before its first column) locates them all.  Per group of kLook chunks: all
+  // bitmap and prefix reads, then the class-sum reads, then the arithmetic, so each kind of
+  // latency is paid once per group.
+  auto rank = [&](int64_t c) {
+    const int wi = static_cast<int>(c >> 5);
+    return pref[wi] + __builtin_popcount(bits[wi] & ((1u << (c & 31)) - 1u));
+  };
+  auto has = [&](int64_t c) { return (bits[c >> 5] >> (c & 31)) & 1u; };
+  auto single = [&](int64_t f) {
+    const int64_t c = f - f0;
+    float g = w * exp2_fast(load_lp(in.log_probs, DT, f) * kLog2e);
+    if (has(c)) g -= acc[rank(c)];
+    store_grad(grad, DT, f, g);
+  };
+  if (f0 + lane < a0) single(f0 + lane);
+  auto batch = [&](int64_t q0) {
+#pragma unroll
+    for (int h = 0; h < RB; h += kLook) {
+      uint32_t m8[kLook];
+      int rk[kLook];
+#pragma unroll
+      for (int u = 0; u < kLook; ++u) {
+        const int64_t c0 = min((q0 + 64 * (h + u)) * 8 - f0, D - 1);
+        const int wi = static_cast<int>(c0 >> 5), sh = static_cast<int>(c0 & 31);
+        const uint32_t b0 = bits[wi], b1 = wi + 1 < Dw ? bits[wi + 1] : 0u;
+        m8[u] = static_cast<uint32_t>((((uint64_t)b1 << 32) | b0) >> sh) & 0xffu;
+        rk[u] = pref[wi] + __builtin_popcount(b0 & ((1u << sh) - 1u));
+      }
+      float c0v[kLook], c1v[kLook];
+#pragma unroll
+      for (int u = 0; u < kLook; ++u) {
+        c0v[u] = acc[rk[u]];  // rank <= U+1: inside this wave's class sums and bitmap
+        c1v[u] = acc[rk[u] + 1];
+      }
+#pragma unroll
+      for (int u = 0; u < kLook; ++u) {
+        const int64_t q = q0 + 64 * (h + u);
+        if (q >= qe) continue;
+        float v[8];
+        unpack8<DT>(raw[h + u], v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = w * exp2_fast(v[e] * kLog2e);
+        uint32_t mm = m8[u];
+        int j = 0;
+        while (mm) {
+          const int e = __builtin_ctz(mm);
+          mm &= mm - 1;
+          v[e] -= j == 0 ? c0v[u] : (j == 1 ? c1v[u] : acc[rk[u] + j]);
+          ++j;
+        }
+        store8<DT>(grad, q, v);
+      }
+    }
+  };
+  if (qe > qb) {
+    batch(qb + lane);
+    for (int64_t q0 = qb + lane + 64 * RB; q0 < qe + lane; q0 += 64 * RB) {  // rows longer than one batch
+#pragma unroll
+      for (int u = 0; u < RB; ++u) raw[u] = ld8<DT>(in.log_probs, min(q0 + 64 * u, qe - 1));
+      batch(q0);
+    }
+  }
+  if (a1 + lane < f1 && a1 + lane >= a0) single(a1 + lane);
+}
+
+}  // namespace rows
+}  // namespace pctc

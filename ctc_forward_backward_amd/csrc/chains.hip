@@ -183,6 +183,8 @@ struct Ctx {
   int* sig;                 // this block's offset per chunk, at the row of the chunk's first frame
   float* ab;                // this block's 128 states per row (row 0)
   int* err;
+  const Inputs* in;
+  int64_t B;
 };
 
 // The recursion of one block, specialised on the direction and on the kinds of its links, so that
@@ -346,6 +348,7 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
       const bool nan = P.meta[cx.b].flags & 1;
       P.nll[cx.b] = nan ? (double)NAN : (feasible ? -log2p * kLn2 : (double)INFINITY);
       P.lsh[cx.b] = (double)off + (double)fin;
+      P.w[cx.b] = utterance_weight(*cx.in, cx.B, cx.b, !nan && !feasible);  // for this group's rows
     } else {
       P.llb[cx.b] = feasible ? log2p : -(double)INFINITY;
     }
@@ -353,8 +356,8 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
 }
 
 // One block (this wave) of segment `seg` of chain (utterance, direction).
-__device__ __forceinline__ void run_wave(const Layout& L, const Pointers& P, Shared& sh, int chain, int seg, int w,
-                                         int lane) {
+__device__ __forceinline__ void run_wave(const Inputs& in, const Layout& L, const Pointers& P, Shared& sh, int chain,
+                                         int seg, int w, int lane) {
   Ctx cx;
   cx.b = chain >> 1;
   const bool beta = chain & 1;
@@ -393,6 +396,10 @@ __device__ __forceinline__ void run_wave(const Layout& L, const Pointers& P, Sha
   cx.sig = P.sig + (dir * Gm + j) * TT;
   cx.ab = P.AB + (dir * Gm + j) * TT * 128;
   cx.err = &P.ctl->err;
+  cx.in = &in;
+  cx.B = L.B;
+  // the recursions are the critical path: their waves win the SIMD over row kernels sharing it
+  __builtin_amdgcn_s_setprio(3);
   if (!beta) {
     if (in_global) {
       if (out_global) run_block<false, true, true>(cx, P);
@@ -410,39 +417,48 @@ __device__ __forceinline__ void run_wave(const Layout& L, const Pointers& P, Sha
       else run_block<true, false, false>(cx, P);
     }
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
-__global__ void __launch_bounds__(256, 1) chain_workers(Layout L, Pointers P) {
+__global__ void __launch_bounds__(256, 1) chain_workers(Inputs in, Layout L, Pointers P, int group) {
   __shared__ Shared sh;
   // the wave index and the claimed item are wave-uniform: say so, so that every address derived
   // from them stays in scalar registers
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qlen = P.ctl->qlen;
+  GroupQ* q = &P.ctl->g[group];
+  const int qlen = q->qlen;
+  const int* items = P.items + q->itemoff;
   for (;;) {
     // a fresh segment: clear the rings (tag 0 matches no frame) and the progress words
     for (int i = tid; i < kWaves * kR; i += 256) (&sh.ring[0][0])[i] = 0ull;
     if (tid < kWaves) sh.prog[tid] = -1;
-    if (tid == 0) sh.item = atomicAdd(&P.ctl->qcount, 1);
+    if (tid == 0) sh.item = atomicAdd(&q->qcount, 1);
     __syncthreads();
     const int idx = __builtin_amdgcn_readfirstlane(sh.item);
     if (idx >= qlen) break;
-    const int item = __builtin_amdgcn_readfirstlane(P.items[idx]);
-    run_wave(L, P, sh, item >> 12, item & 4095, w, lane);
+    const int item = __builtin_amdgcn_readfirstlane(items[idx]);
+    run_wave(in, L, P, sh, item >> 12, item & 4095, w, lane);
     __syncthreads();
   }
 }
 
 }  // namespace
 
-hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {
-  (void)in;
+// LDS a workgroup reserves beyond its rings, so that no compute unit ever holds two of them: the
+// recursions of different groups run on different compute units, sharing each only with row work
+constexpr size_t kChainReserve = 96 * 1024;
+
+hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s) {
   if (L.B == 0 || L.T_total == 0) return hipGetLastError();
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&chain_workers), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(kChainReserve));
   if (e != hipSuccess) return e;
-  // one workgroup (a segment of four waves, one per SIMD) per compute unit
-  chain_workers<<<cus > 0 ? cus : 256, 256, 0, s>>>(L, P);
+  // at most one workgroup (a segment of four waves, one per SIMD) per compute unit
+  chain_workers<<<cus > 0 ? cus : 256, 256, kChainReserve, s>>>(in, L, P, group);
   return hipGetLastError();
 }
 

@@ -49,16 +49,35 @@ struct Layout {
   int64_t Gmax;      // state-pair blocks of the longest target: ceil((Umax + 1) / 64)
   int64_t Dw;        // 32-bit words of a class bitmap: ceil(D / 32)
   int64_t C_stride;  // floats per row of the compact class sums (>= Umax + 1)
-  size_t off_cbits, off_cpref, off_dmap, off_meta, off_lab, off_rowmap, off_rowoff, off_E, off_AB, off_nll, off_llb, off_lsh, off_w, off_post, off_ring, off_nring,
+  size_t off_cbits, off_cpref, off_dmap, off_meta, off_lab, off_rowmap, off_rowoff, off_E, off_AB, off_nll, off_llb, off_lsh, off_w, off_post, off_order, off_cum, off_ring, off_nring,
       off_sig, off_items, off_ctl, total;
 };
 
-// control words of the recursion work queue
+// Utterances are sorted by frame count (longest first) and cut into up to kMaxGroups groups of
+// consecutive sorted positions; each group runs its gather, recursions and rows on a stream of its
+// own, so the rows of short utterances overlap the recursions of long ones.  Three streams (the
+// caller's and two more) fit the hardware queues a process gets by default; group g ends where the
+// groups so far hold kGroupShare[K-1][g] of the rows, so that the group of the longest recursion
+// has few rows left to do after it.
+constexpr int kMaxGroups = 3;
+
+// the work of one group
+struct GroupQ {
+  int qlen;     // recursion segments of the group
+  int qcount;   // next segment to claim
+  int itemoff;  // first segment of the group in the segment list
+  int first;    // first sorted position of the group
+  int count;    // utterances in the group
+  int nrows;    // rows owned by the group's utterances
+  int pad[2];
+};
+
+// control words of the recursion work queues
 struct ChainCtl {
-  int qlen;    // number of queued blocks
-  int qcount;  // next block to claim
-  int err;     // non-zero: a block gave up waiting for its neighbour (results unspecified)
-  int pad[61];
+  int err;      // non-zero: a block gave up waiting for its neighbour (results unspecified)
+  int ngroups;
+  int pad[6];
+  GroupQ g[kMaxGroups];
 };
 
 Layout make_layout(int64_t T_total, int64_t D, int64_t B, int64_t Umax);
@@ -80,7 +99,9 @@ struct Pointers {
   unsigned long long* ring;  // (2, Gmax, T_total) block-boundary values (value, offset) per frame
   unsigned long long* nring; // (T_total,) a written (-inf, offset 0) slot everywhere: the neighbour of an edge block
   int* sig;      // (2, Gmax, T_total) integer offset of each block's stored values, per chunk
-  int* items;    // (2 B Gmax) queued recursion blocks: (utterance * 2 + direction) << 12 | block
+  int* items;    // (2 B Gmax) queued recursion segments, by group: (utterance * 2 + direction) << 12 | segment
+  int* order;    // (B) utterances by frame count, longest first (ties by index)
+  int* cum;      // (B) per sorted position: rows of the group's earlier utterances
   ChainCtl* ctl;
   // classes of each utterance's extended labels (blank and labels), for the gradient rows:
   uint32_t* cbits;  // (B, Dw) bitmap of the classes present
@@ -135,6 +156,39 @@ __device__ __forceinline__ void store_grad(void* p, int dtype, int64_t i, float 
 
 __device__ __forceinline__ int64_t load_index(const void* p, bool i64, int64_t i) {
   return i64 ? static_cast<const int64_t*>(p)[i] : static_cast<int64_t>(static_cast<const int32_t*>(p)[i]);
+}
+
+// The rows of group g as one list (its utterances in sorted order, each utterance's rows in order):
+// fn(r, b) for list entries [j0, j1).  Everything here is uniform over the wave.
+template <typename F>
+__device__ __forceinline__ void group_rows(const Pointers& P, int g, int64_t j0, int64_t j1, F fn) {
+  const GroupQ& q = P.ctl->g[g];
+  if (j0 >= j1 || q.count <= 0) return;
+  // the last sorted position whose first list entry is at or before j0
+  int lo = q.first, hi = q.first + q.count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (P.cum[mid] <= j0) lo = mid;
+    else hi = mid - 1;
+  }
+  int64_t j = j0;
+  for (int i = lo; j < j1 && i < q.first + q.count; ++i) {
+    const int b = __builtin_amdgcn_readfirstlane(P.order[i]);
+    const Meta m = P.meta[b];
+    const int64_t off = j - P.cum[i];  // row of the utterance
+    const int64_t take = min(j1 - j, (int64_t)m.T - off);
+    for (int64_t k = 0; k < take; ++k) fn(m.start + off + k, b);
+    if (take > 0) j += take;
+  }
+}
+
+// list entries [j0, j1) of wave `wid` out of `waves` over group g's rows
+__device__ __forceinline__ void wave_share(const Pointers& P, int g, int64_t wid, int64_t waves, int64_t& j0,
+                                           int64_t& j1) {
+  const int64_t n = P.ctl->g[g].nrows;
+  const int64_t per = (n + waves - 1) / waves;
+  j0 = min(wid * per, n);
+  j1 = min(j0 + per, n);
 }
 
 // ---- 8-element chunks of a (T_total, D) log-prob / gradient buffer ----------------------------
@@ -301,15 +355,29 @@ struct Inputs {
   const float* grad_scale;
 };
 
+// The gradient weight of utterance b: grad_scale[b] (or 1), over B * max(U, 1) for the mean (U as
+// the caller gave it), and 0 under zero_infinity for an utterance without alignment.
+__device__ __forceinline__ float utterance_weight(const Inputs& in, int64_t B, int64_t b, bool infinite) {
+  const int64_t U = load_index(in.target_lengths, in.index_flags & 8, b);
+  const double Uc = U > 1 ? (double)U : 1.0;
+  double w = in.grad_scale ? (double)in.grad_scale[b] : 1.0;
+  if (in.reduction == 2) w /= (double)B * Uc;
+  if (in.zero_infinity && infinite) w = 0.0;
+  return static_cast<float>(w);
+}
+
 hipError_t launch_prep(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
-hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
-hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
-hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
+hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s);
+// sorts the utterances and cuts them into `groups` groups (see GroupQ)
+hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P, int groups, hipStream_t s);
+hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s);
 hipError_t launch_weights(const Inputs& in, const Layout& L, const Pointers& P, float* losses_out, float* reduced_out,
                           hipStream_t s);
 hipError_t launch_classes(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
-hipError_t launch_posteriors(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
-hipError_t launch_dense(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s);
+hipError_t launch_posteriors(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s);
+hipError_t launch_dense(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, int group, hipStream_t s);
+// zero gradient rows owned by no utterance
+hipError_t launch_gaps(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 hipError_t launch_zero_bytes(void* p, int64_t nbytes, hipStream_t s);
 hipError_t launch_reduce(const float* losses, const void* target_lengths, bool i64, int64_t B, int reduction, float* out,

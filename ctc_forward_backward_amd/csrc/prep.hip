@@ -88,17 +88,16 @@ __device__ __forceinline__ float ld1(const void* p, int64_t i) {
 }
 
 template <int DT>
-__global__ void __launch_bounds__(256) gather_kernel(Inputs in, Layout L, Pointers P, int rows_per_wave) {
+__global__ void __launch_bounds__(256) gather_kernel(Inputs in, Layout L, Pointers P, int group) {
   const int lane = threadIdx.x & 63;
   const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t r0 = wid * rows_per_wave, r1 = min(r0 + rows_per_wave, L.T_total);
+  int64_t j0, j1;
+  wave_share(P, group, wid, (int64_t)gridDim.x * 4, j0, j1);
   const int64_t D = L.D;
   int cur_b = -1, U = 0;
   const int* lab = nullptr;
   int col[kGLab];
-  for (int64_t r = r0; r < r1; ++r) {
-    const int b = __builtin_amdgcn_readfirstlane(P.rowmap[r]);
-    if (b < 0) continue;
+  group_rows(P, group, j0, j1, [&](int64_t r, int b) {
     if (b != cur_b) {
       U = P.meta[b].U;
       lab = P.lab + (int64_t)b * (L.Umax + 1);
@@ -144,7 +143,7 @@ __global__ void __launch_bounds__(256) gather_kernel(Inputs in, Layout L, Pointe
     }
     if (lane == 0) E[U + 1] = kNeg;  // the column of label states that do not exist
     if (nan) atomicOr(&P.meta[b].flags, 1);
-  }
+  });
 }
 
 // One workgroup per utterance: the bitmap of the classes its extended labels use (the blank and
@@ -260,7 +259,7 @@ __global__ void __launch_bounds__(256) reduce_kernel(const float* losses, const 
 // segments in producer order (last segment first).  A segment only ever waits on its producer,
 // which sits earlier in the queue, so segments claimed in queue order can always finish.
 // Frameless utterances get their loss here.
-__global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, int sort) {
+__global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, int sort, int groups) {
   extern __shared__ int sh[];  // sort ? [T (B) | order (B)] : unused
   const int B = static_cast<int>(L.B);
   const int tid = threadIdx.x, nt = blockDim.x;
@@ -280,6 +279,7 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
     }
     __syncthreads();
   }
+  for (int i = tid; i < B; i += nt) P.order[i] = sort ? sh[B + i] : i;
   for (int b = tid; b < B; b += nt) {
     const Meta m = P.meta[b];
     if (m.T == 0) {
@@ -288,21 +288,49 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
     }
   }
   if (tid == 0) {
-    int n = 0;
-    for (int i = 0; i < B; ++i) {
-      const int b = sort ? sh[B + i] : i;
-      const Meta m = P.meta[b];
-      if (m.T == 0) continue;
-      // segments of four 64-pair blocks
-      const int nseg = (((m.U + 1 + 63) >> 6) + 3) >> 2;
-      for (int j = 0; j < nseg; ++j) {
-        P.items[n++] = ((2 * b) << 12) | j;
-        P.items[n++] = ((2 * b + 1) << 12) | (nseg - 1 - j);
+    // group g ends where the groups so far hold the share of the rows below (each group at least one
+    // utterance); its segments in sorted order, each utterance's producers first
+    const float share[kMaxGroups][kMaxGroups] = {{1.0f, 1.0f, 1.0f}, {0.15f, 1.0f, 1.0f}, {0.1f, 0.4f, 1.0f}};
+    int64_t total = 0;
+    for (int i = 0; i < B; ++i) total += P.meta[sort ? sh[B + i] : i].T;
+    int n = 0, pos = 0;
+    int64_t done = 0;
+    for (int g = 0; g < kMaxGroups; ++g) {
+      GroupQ q{};
+      if (g < groups) {
+        const int p0 = pos;
+        const int64_t goal = g == groups - 1 ? total : static_cast<int64_t>(share[groups - 1][g] * (double)total);
+        int p1 = p0;
+        const int keep = groups - 1 - g;  // utterances to leave for the groups after this one
+        do {
+          done += P.meta[sort ? sh[B + p1] : p1].T;
+          ++p1;
+        } while (p1 < B - keep && (done < goal || g == groups - 1));
+        q.itemoff = n;
+        q.first = p0;
+        q.count = p1 - p0;
+        int rows = 0;
+        for (int i = p0; i < p1; ++i) {
+          const int b = sort ? sh[B + i] : i;
+          const Meta m = P.meta[b];
+          P.cum[i] = rows;
+          rows += m.T;
+          if (m.T == 0) continue;
+          // segments of four 64-pair blocks
+          const int nseg = (((m.U + 1 + 63) >> 6) + 3) >> 2;
+          for (int j = 0; j < nseg; ++j) {
+            P.items[n++] = ((2 * b) << 12) | j;
+            P.items[n++] = ((2 * b + 1) << 12) | (nseg - 1 - j);
+          }
+        }
+        q.qlen = n - q.itemoff;
+        q.nrows = rows;
+        pos = p1;
       }
+      P.ctl->g[g] = q;
     }
-    P.ctl->qlen = n;
-    P.ctl->qcount = 0;
     P.ctl->err = 0;
+    P.ctl->ngroups = groups;
   }
 }
 
@@ -322,21 +350,17 @@ hipError_t launch_prep(const Inputs& in, const Layout& L, const Pointers& P, hip
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {
+hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s) {
   if (L.T_total == 0 || L.B == 0) return hipGetLastError();
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  // about 32 waves per compute unit, each on a contiguous range of rows
-  const int64_t waves = 32 * (int64_t)(cus > 0 ? cus : 256);
-  const int64_t rpw = (L.T_total + waves - 1) / waves;
-  const int64_t wanted_waves = (L.T_total + rpw - 1) / rpw;
-  const int grid = static_cast<int>((wanted_waves + 3) / 4);
-  const int rows = static_cast<int>(rpw);
-  if (in.dtype == kF32) gather_kernel<kF32><<<grid, 256, 0, s>>>(in, L, P, rows);
-  else if (in.dtype == kF16) gather_kernel<kF16><<<grid, 256, 0, s>>>(in, L, P, rows);
-  else gather_kernel<kBF16><<<grid, 256, 0, s>>>(in, L, P, rows);
+  // about 32 waves per compute unit; each takes a contiguous share of the group's rows
+  const int grid = 8 * (cus > 0 ? cus : 256);
+  if (in.dtype == kF32) gather_kernel<kF32><<<grid, 256, 0, s>>>(in, L, P, group);
+  else if (in.dtype == kF16) gather_kernel<kF16><<<grid, 256, 0, s>>>(in, L, P, group);
+  else gather_kernel<kBF16><<<grid, 256, 0, s>>>(in, L, P, group);
   return hipGetLastError();
 }
 
@@ -353,9 +377,12 @@ hipError_t launch_classes(const Inputs& in, const Layout& L, const Pointers& P, 
   return hipGetLastError();
 }
 
-hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {
+hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P, int groups, hipStream_t s) {
   (void)in;
-  if (L.B == 0) return hipGetLastError();
+  if (L.B == 0) {  // nothing to queue: the control words still start clean for the status read
+    zero_u32_kernel<<<1, 256, 0, s>>>(reinterpret_cast<uint32_t*>(P.ctl), sizeof(ChainCtl) / 4);
+    return hipGetLastError();
+  }
   // every ring slot starts unwritten (zero: the written mark 0x80 of its high word is clear); a
   // block publishes (value, offset << 8 | 0x80 | tag) into it once
   const int64_t words = 2 * 2 * L.Gmax * L.T_total;
@@ -370,7 +397,7 @@ hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  schedule_kernel<<<1, 1024, lds, s>>>(L, P, sort);
+  schedule_kernel<<<1, 1024, lds, s>>>(L, P, sort, groups);
   return hipGetLastError();
 }
 

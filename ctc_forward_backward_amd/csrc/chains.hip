@@ -28,7 +28,7 @@
 //     A slot holds the value and, in its high word, the producer's integer offset and a validity
 //     mark (the LDS ring also tags the chunk, since its slots are reused).  Nobody waits on a later
 //     block, so the pipeline has no round trip per frame, only a fill latency per block.
-//   - A consumer takes the neighbour values of a whole 16-frame chunk at the chunk's start, one per
+//   - A consumer takes the neighbour values of a whole 32-frame chunk at the chunk's start, one per
 //     lane, checks them with one ballot and converts them to its own offset; a frame then costs one
 //     v_readlane.  Global slots are loaded one chunk ahead.
 //   - Segments are items of one work queue, producers first (see the schedule kernel), claimed by
@@ -50,7 +50,7 @@ namespace pctc {
 namespace {
 
 constexpr int kK = kChunk;             // frames per chunk (prefetch depth and renormalisation period)
-constexpr int kR = 128;                // LDS ring slots per wave boundary (8 chunks)
+constexpr int kR = 128;                // LDS ring slots per wave boundary (4 chunks)
 constexpr int kWaves = 4;              // blocks per segment = waves per workgroup
 constexpr int kSpinLimit = 1 << 20;    // polls before a wave gives up waiting (about a second)
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
@@ -239,25 +239,25 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
       for (int i = 0; i < kK; ++i)
         el[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(er, cx.eidx * 4, in_chunk(i) * Es * 4, 0));
     }
-    const int l16 = lane & (kK - 1);
-    float ebv = P.E[row(1 + l16) * Es];
+    const int lk = lane & (kK - 1);
+    float ebv = P.E[row(1 + lk) * Es];
     unsigned long long hraw = 0;
-    if (IN_GLOBAL) hraw = gload(cx.gin + row(min(l16, nsteps)));
+    if (IN_GLOBAL) hraw = gload(cx.gin + row(min(lk, nsteps)));
 
     auto run_chunk = [&](auto full, int c, int nvalid) {
       constexpr bool FULL = decltype(full)::value;
       // neighbour values of this chunk: lane i < kK holds the producer's frame at step c*kK + i
       const bool need = lane < (FULL ? kK : nvalid);
       const int want = lane == 0 ? c - 1 : c;
-      const unsigned long long* lp = cx.lin + ((c * kK + l16 - 1) & (kR - 1));
+      const unsigned long long* lp = cx.lin + ((c * kK + lk - 1) & (kR - 1));
       unsigned long long raw = IN_GLOBAL ? hraw : lload(lp);
       const bool check_cons = !OUT_GLOBAL && cx.lout_live && c >= kR / kK - 1;
       const int cons = check_cons ? __hip_atomic_load(cx.prog_cons, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0;
-      const float ebn = P.E[row(1 + (int64_t)(c + 1) * kK + l16) * Es];
+      const float ebn = P.E[row(1 + (int64_t)(c + 1) * kK + lk) * Es];
       cx.sig[row(1 + (int64_t)c * kK)] = static_cast<int>(off);
       if (IN_GLOBAL) {
-        if (__ballot(need && !global_ok(raw))) raw = wait_global(cx.gin + row(min(c * kK + l16, nsteps)), raw, need, err);
-        hraw = gload(cx.gin + row(min((c + 1) * kK + l16, nsteps)));
+        if (__ballot(need && !global_ok(raw))) raw = wait_global(cx.gin + row(min(c * kK + lk, nsteps)), raw, need, err);
+        hraw = gload(cx.gin + row(min((c + 1) * kK + lk, nsteps)));
       } else {
         if (__ballot(need && !lds_ok(raw, want))) raw = wait_lds(lp, raw, need, want, err);
         if (lane == 0) __hip_atomic_store(cx.prog_self, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -444,9 +444,10 @@ __global__ void __launch_bounds__(256, 1) chain_workers(Inputs in, Layout L, Poi
 
 }  // namespace
 
-// LDS a workgroup reserves beyond its rings, so that no compute unit ever holds two of them: the
-// recursions of different groups run on different compute units, sharing each only with row work
-constexpr size_t kChainReserve = 96 * 1024;
+// LDS a workgroup reserves beyond its rings: nearly all of a compute unit's 160 KB, so that no compute
+// unit holds two recursion workgroups and no row kernel (each takes some LDS) shares a SIMD with a
+// recursion wave -- a streaming wave beside it more than doubles its time per frame
+constexpr size_t kChainReserve = 152 * 1024;
 
 hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s) {
   if (L.B == 0 || L.T_total == 0) return hipGetLastError();

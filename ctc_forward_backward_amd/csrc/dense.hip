@@ -8,6 +8,8 @@
 // Design for gfx950: one wave per row, each wave on a contiguous share of the group's rows (its
 // utterance, and the class bitmap in LDS, rarely change); the latency-bound posterior kernel runs at
 // high occupancy, the gradient kernel streams whole rows.
+#include <algorithm>
+
 #include "rows.h"
 
 namespace pctc {
@@ -77,7 +79,7 @@ hipError_t launch_posteriors(const Inputs& in, const Layout& L, const Pointers& 
   if (L.T_total == 0 || L.B == 0) return hipGetLastError();
   // per wave: the class sums (U+1, rounded to 4); as many waves as fit, each on a contiguous share
   const int per_wave = static_cast<int>(L.C_stride);
-  const size_t lds = 4 * sizeof(float) * (size_t)per_wave;
+  const size_t lds = std::max(4 * sizeof(float) * (size_t)per_wave, kRowKernelLds);
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&posterior_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (err != hipSuccess) return err;
@@ -91,7 +93,7 @@ hipError_t launch_dense(const Inputs& in, const Layout& L, const Pointers& P, vo
   if (L.T_total == 0 || L.D == 0 || L.B == 0) return hipGetLastError();
   // per wave: the class sums (U+1, rounded to 4), the class bitmap and its prefix counts
   const int per_wave = static_cast<int>(L.C_stride + 2 * L.Dw);
-  const size_t lds = 4 * sizeof(uint32_t) * (size_t)per_wave;
+  const size_t lds = std::max(4 * sizeof(uint32_t) * (size_t)per_wave, kRowKernelLds);
   auto launch = [&](auto kernel) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));

@@ -37,11 +37,15 @@ struct Meta {
 // Workspace carve-up.  Every region is 256-byte aligned.
 // Frames per chunk of the recursions: their prefetch depth and the period of their integer shift.
 // A block's offset is stored once per chunk, at the row of the chunk's first frame.
-constexpr int kChunk = 16;
+constexpr int kChunk = 32;
+
+// Least LDS a row kernel takes per workgroup: with the recursion workgroups' reservation it keeps
+// the two kinds of workgroup off each other's compute units.
+constexpr size_t kRowKernelLds = 8 * 1024;
 
 // Rows of padding before and after the emission table: the recursions prefetch up to two chunks
 // of frames past either end of an utterance without clamping.
-constexpr int kEPad = 40;
+constexpr int kEPad = 72;
 
 struct Layout {
   int64_t T_total, D, B, Umax;

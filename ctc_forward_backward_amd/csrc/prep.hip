@@ -356,11 +356,14 @@ hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, i
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  // about 32 waves per compute unit; each takes a contiguous share of the group's rows
+  // about 32 waves per compute unit; each takes a contiguous share of the group's rows.  The kernel
+  // uses no LDS, but takes some so that it is never placed beside a recursion workgroup (which
+  // reserves the rest of a compute unit's LDS)
   const int grid = 8 * (cus > 0 ? cus : 256);
-  if (in.dtype == kF32) gather_kernel<kF32><<<grid, 256, 0, s>>>(in, L, P, group);
-  else if (in.dtype == kF16) gather_kernel<kF16><<<grid, 256, 0, s>>>(in, L, P, group);
-  else gather_kernel<kBF16><<<grid, 256, 0, s>>>(in, L, P, group);
+  const size_t lds = kRowKernelLds;
+  if (in.dtype == kF32) gather_kernel<kF32><<<grid, 256, lds, s>>>(in, L, P, group);
+  else if (in.dtype == kF16) gather_kernel<kF16><<<grid, 256, lds, s>>>(in, L, P, group);
+  else gather_kernel<kBF16><<<grid, 256, lds, s>>>(in, L, P, group);
   return hipGetLastError();
 }
 

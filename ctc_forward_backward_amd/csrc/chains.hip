@@ -40,7 +40,8 @@
 //     (block, chunk) and summed in float64 for the loss.
 //   - Per frame a wave issues one 512-byte store of its 128 states (a block-major time series) and
 //     one load of next chunk's label emission, both through buffer resources rebased per chunk so
-//     that every offset is a scalar register; the blank emission of a chunk is one load per lane.
+//     that every offset is a scalar register; the blank emissions of a chunk are one contiguous load,
+//     one frame per lane.
 #include <type_traits>
 
 #include "pctc_internal.h"
@@ -51,7 +52,8 @@ namespace {
 
 constexpr int kK = kChunk;             // frames per chunk (prefetch depth and renormalisation period)
 constexpr int kR = 128;                // LDS ring slots per wave boundary (4 chunks)
-constexpr int kWaves = 4;              // blocks per segment = waves per workgroup
+constexpr int kWaves = kSegWaves;      // blocks per segment = waves per workgroup
+constexpr int kThreads = 64 * kWaves;
 constexpr int kSpinLimit = 1 << 20;    // polls before a wave gives up waiting (about a second)
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
 static_assert(2 * kK + 1 <= kEPad, "emission padding must cover two chunks of prefetch");
@@ -171,6 +173,7 @@ struct Ctx {
   int b, T, U, j, k, lane;
   int64_t start;
   bool vl, sk;
+  bool no_in;               // no producer: every neighbour slot is (-inf, offset 0), nothing to load
   int eidx;                 // this lane's label column in the emission table (U+1: the -1e30 column)
   int64_t Es;               // floats per emission row
   const unsigned long long* gin;  // global ring read by this block (row-indexed)
@@ -209,7 +212,7 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
   float xb, xl, off = 0.0f;
   {
     const int64_t r = row(0);
-    const float eb = P.E[r * Es];
+    const float eb = P.Eb[r];
     const float el = P.E[r * Es + cx.eidx];
     const bool first = BETA ? (k == U) : (k == 0);
     xb = first ? eb : kNeg;
@@ -225,7 +228,7 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
   const int nsteps = T - 1;
   if (nsteps > 0) {
     // build a lead over a producer in another segment: its slots are loaded a chunk ahead
-    if (IN_GLOBAL) {
+    if (IN_GLOBAL && !cx.no_in) {
       const unsigned long long* p = cx.gin + row(min(2 * kK, T - 1));
       wait_global(p, gload(p), true, err);
     }
@@ -240,9 +243,10 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
         el[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(er, cx.eidx * 4, in_chunk(i) * Es * 4, 0));
     }
     const int lk = lane & (kK - 1);
-    float ebv = P.E[row(1 + lk) * Es];
+    float ebv = P.Eb[row(1 + lk)];
+    const unsigned long long none = pack(kNeg, 0x80u);
     unsigned long long hraw = 0;
-    if (IN_GLOBAL) hraw = gload(cx.gin + row(min(lk, nsteps)));
+    if (IN_GLOBAL) hraw = cx.no_in ? none : gload(cx.gin + row(min(lk, nsteps)));
 
     auto run_chunk = [&](auto full, int c, int nvalid) {
       constexpr bool FULL = decltype(full)::value;
@@ -253,11 +257,11 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
       unsigned long long raw = IN_GLOBAL ? hraw : lload(lp);
       const bool check_cons = !OUT_GLOBAL && cx.lout_live && c >= kR / kK - 1;
       const int cons = check_cons ? __hip_atomic_load(cx.prog_cons, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0;
-      const float ebn = P.E[row(1 + (int64_t)(c + 1) * kK + lk) * Es];
+      const float ebn = P.Eb[row(1 + (int64_t)(c + 1) * kK + lk)];
       cx.sig[row(1 + (int64_t)c * kK)] = static_cast<int>(off);
       if (IN_GLOBAL) {
         if (__ballot(need && !global_ok(raw))) raw = wait_global(cx.gin + row(min(c * kK + lk, nsteps)), raw, need, err);
-        hraw = gload(cx.gin + row(min((c + 1) * kK + lk, nsteps)));
+        hraw = cx.no_in ? none : gload(cx.gin + row(min((c + 1) * kK + lk, nsteps)));
       } else {
         if (__ballot(need && !lds_ok(raw, want))) raw = wait_lds(lp, raw, need, want, err);
         if (lane == 0) __hip_atomic_store(cx.prog_self, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -327,7 +331,7 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
     const int step = T - 1;
     if (IN_GLOBAL) {
       const unsigned long long* p = cx.gin + row(step);
-      h = slot_value(wait_global(p, gload(p), true, err), off);
+      h = cx.no_in ? kNeg : slot_value(wait_global(p, gload(p), true, err), off);
     } else {
       const unsigned long long* p = cx.lin + ((step - 1) & (kR - 1));
       h = slot_value(wait_lds(p, lload(p), true, chunk_of(step), err), off);
@@ -385,7 +389,9 @@ __device__ __forceinline__ void run_wave(const Inputs& in, const Layout& L, cons
   const bool out_global = has_out && (beta ? (w == 0) : (w == kWaves - 1));
   const int dir = beta ? 1 : 0;
   const int64_t Gm = L.Gmax, TT = L.T_total;
-  cx.gin = has_in ? P.ring + (dir * Gm + (beta ? j + 1 : j - 1)) * TT : P.nring;
+  cx.no_in = !has_in;
+  const int64_t jin = has_in ? (beta ? j + 1 : j - 1) : j;  // without a producer the slab is never read
+  cx.gin = P.ring + (dir * Gm + jin) * TT;
   cx.gout = P.ring + (dir * Gm + j) * TT;
   // LDS ring[w] links waves w and w+1 (alpha) or w+1 and w (beta); ring[kWaves-1] is a sink
   cx.lin = sh.ring[beta ? min(w, kWaves - 2) : max(w - 1, 0)];
@@ -420,7 +426,7 @@ __device__ __forceinline__ void run_wave(const Inputs& in, const Layout& L, cons
   __builtin_amdgcn_s_setprio(0);
 }
 
-__global__ void __launch_bounds__(256, 1) chain_workers(Inputs in, Layout L, Pointers P, int group) {
+__global__ void __launch_bounds__(kThreads, 1) chain_workers(Inputs in, Layout L, Pointers P, int group) {
   __shared__ Shared sh;
   // the wave index and the claimed item are wave-uniform: say so, so that every address derived
   // from them stays in scalar registers
@@ -430,7 +436,7 @@ __global__ void __launch_bounds__(256, 1) chain_workers(Inputs in, Layout L, Poi
   const int* items = P.items + q->itemoff;
   for (;;) {
     // a fresh segment: clear the rings (tag 0 matches no frame) and the progress words
-    for (int i = tid; i < kWaves * kR; i += 256) (&sh.ring[0][0])[i] = 0ull;
+    for (int i = tid; i < kWaves * kR; i += kThreads) (&sh.ring[0][0])[i] = 0ull;
     if (tid < kWaves) sh.prog[tid] = -1;
     if (tid == 0) sh.item = atomicAdd(&q->qcount, 1);
     __syncthreads();
@@ -448,6 +454,8 @@ __global__ void __launch_bounds__(256, 1) chain_workers(Inputs in, Layout L, Poi
 // unit holds two recursion workgroups and no row kernel (each takes some LDS) shares a SIMD with a
 // recursion wave -- a streaming wave beside it more than doubles its time per frame
 constexpr size_t kChainReserve = 152 * 1024;
+static_assert(kChainReserve + sizeof(Shared) <= 160 * 1024 && kChainReserve + sizeof(Shared) + kRowKernelLds > 160 * 1024,
+              "one recursion workgroup per compute unit, alone");
 
 hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s) {
   if (L.B == 0 || L.T_total == 0) return hipGetLastError();
@@ -459,7 +467,7 @@ hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, i
                             static_cast<int>(kChainReserve));
   if (e != hipSuccess) return e;
   // at most one workgroup (a segment of four waves, one per SIMD) per compute unit
-  chain_workers<<<cus > 0 ? cus : 256, 256, kChainReserve, s>>>(in, L, P, group);
+  chain_workers<<<cus > 0 ? cus : 256, kThreads, kChainReserve, s>>>(in, L, P, group);
   return hipGetLastError();
 }
 

@@ -39,6 +39,11 @@ struct Meta {
 // A block's offset is stored once per chunk, at the row of the chunk's first frame.
 constexpr int kChunk = 32;
 
+// 64-pair state blocks per segment of a recursion: the waves of one workgroup, one per SIMD, linked
+// through LDS; segments link through a global ring.  (Two recursion waves on one SIMD slow both more
+// than a global link costs.)
+constexpr int kSegWaves = 4;
+
 // Least LDS a row kernel takes per workgroup: with the recursion workgroups' reservation it keeps
 // the two kinds of workgroup off each other's compute units.
 constexpr size_t kRowKernelLds = 8 * 1024;
@@ -53,7 +58,7 @@ struct Layout {
   int64_t Gmax;      // state-pair blocks of the longest target: ceil((Umax + 1) / 64)
   int64_t Dw;        // 32-bit words of a class bitmap: ceil(D / 32)
   int64_t C_stride;  // floats per row of the compact class sums (>= Umax + 1)
-  size_t off_cbits, off_cpref, off_dmap, off_meta, off_lab, off_rowmap, off_rowoff, off_E, off_AB, off_nll, off_llb, off_lsh, off_w, off_post, off_order, off_cum, off_ring, off_nring,
+  size_t off_cbits, off_cpref, off_dmap, off_meta, off_lab, off_rowmap, off_rowoff, off_E, off_Eb, off_AB, off_nll, off_llb, off_lsh, off_w, off_post, off_order, off_cum, off_ring,
       off_sig, off_items, off_ctl, total;
 };
 
@@ -92,6 +97,7 @@ struct Pointers {
   int* rowmap;   // (T_total,): owning utterance or -1
   int* rowoff;   // (T_total,): integer offset subtracted from the row's gathered log2 emissions
   float* E;      // (T_total, E_stride): columns 0..U the labels, U+1 holds -1e30; kEPad rows of padding on either side
+  float* Eb;     // (T_total,): column 0 of E (the blank) again, contiguous for the recursions; kEPad padding each side
   // (2, Gmax, T_total, 128): normalised log2 alpha (direction 0) and beta (direction 1) per block
   // of 64 state pairs and per row.  Alpha pair k sits at 2k, 2k+1 (states 2k, 2k+1); beta pair k at
   // 2k, 2k+1 (states 2k-1, 2k), i.e. beta of state s at position s+1, all relative to the block.
@@ -101,7 +107,6 @@ struct Pointers {
   double* lsh;   // (B,) log2 likelihood from the alpha side without the row offsets
   float* w;      // (B,) gradient weight
   unsigned long long* ring;  // (2, Gmax, T_total) block-boundary values (value, offset) per frame
-  unsigned long long* nring; // (T_total,) a written (-inf, offset 0) slot everywhere: the neighbour of an edge block
   int* sig;      // (2, Gmax, T_total) integer offset of each block's stored values, per chunk
   int* items;    // (2 B Gmax) queued recursion segments, by group: (utterance * 2 + direction) << 12 | segment
   int* order;    // (B) utterances by frame count, longest first (ties by index)

@@ -16,10 +16,6 @@ __global__ void fill_i32_kernel(int* p, int64_t n, int v) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
-__global__ void fill_u64_kernel(unsigned long long* p, int64_t n, unsigned long long v) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
-}
-
 __global__ void fill_f32_kernel(float* p, int64_t n, float v) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
 }
@@ -141,7 +137,10 @@ __global__ void __launch_bounds__(256) gather_kernel(Inputs in, Layout L, Pointe
       for (int j = lane; j <= U; j += 64) E[j] -= off;
       if (lane == 0) P.rowoff[r] = static_cast<int>(off);
     }
-    if (lane == 0) E[U + 1] = kNeg;  // the column of label states that do not exist
+    if (lane == 0) {
+      E[U + 1] = kNeg;  // the column of label states that do not exist
+      P.Eb[r] = E[0];   // (this lane wrote E[0] above)
+    }
     if (nan) atomicOr(&P.meta[b].flags, 1);
   });
 }
@@ -255,7 +254,7 @@ __global__ void __launch_bounds__(256) reduce_kernel(const float* losses, const 
 
 // Work queue of the recursions (one workgroup).  Utterances are ordered by frame count, longest
 // first, so that the longest chains start first; each utterance contributes its alpha segments
-// (four 64-pair state blocks each) in producer order (segment 0 first) interleaved with its beta
+// (kSegWaves 64-pair state blocks each) in producer order (segment 0 first) interleaved with its beta
 // segments in producer order (last segment first).  A segment only ever waits on its producer,
 // which sits earlier in the queue, so segments claimed in queue order can always finish.
 // Frameless utterances get their loss here.
@@ -316,8 +315,8 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
           P.cum[i] = rows;
           rows += m.T;
           if (m.T == 0) continue;
-          // segments of four 64-pair blocks
-          const int nseg = (((m.U + 1 + 63) >> 6) + 3) >> 2;
+          // segments of kSegWaves 64-pair blocks
+          const int nseg = (((m.U + 1 + 63) >> 6) + kSegWaves - 1) / kSegWaves;
           for (int j = 0; j < nseg; ++j) {
             P.items[n++] = ((2 * b) << 12) | j;
             P.items[n++] = ((2 * b + 1) << 12) | (nseg - 1 - j);
@@ -390,9 +389,6 @@ hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P,
   // block publishes (value, offset << 8 | 0x80 | tag) into it once
   const int64_t words = 2 * 2 * L.Gmax * L.T_total;
   if (words > 0) fill_i32_kernel<<<grid_for(words, 256), 256, 0, s>>>(reinterpret_cast<int*>(P.ring), words, 0);
-  // the neighbour of an edge block: (-inf, offset 0, written) in every slot
-  const unsigned long long none = (unsigned long long)__builtin_bit_cast(uint32_t, kNeg) | (0x80ull << 32);
-  if (L.T_total > 0) fill_u64_kernel<<<grid_for(L.T_total, 256), 256, 0, s>>>(P.nring, L.T_total, none);
   const int sort = L.B <= 8192 ? 1 : 0;
   const size_t lds = sort ? 2 * sizeof(int) * (size_t)L.B : 0;
   if (lds > 48 * 1024) {

@@ -217,7 +217,10 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
     const bool first = BETA ? (k == U) : (k == 0);
     xb = first ? eb : kNeg;
     xl = (first && cx.vl) ? el : kNeg;
-    *reinterpret_cast<float2*>(cx.ab + r * 128 + 2 * lane) = BETA ? make_float2(xl, xb) : make_float2(xb, xl);
+    // beta is stored without the frame's own emission (the empty sum 0 at its start states), so that
+    // alpha + stored beta is the posterior's exponent with no emission to take out
+    *reinterpret_cast<float2*>(cx.ab + r * 128 + 2 * lane) =
+        BETA ? make_float2((first && cx.vl) ? 0.0f : kNeg, first ? 0.0f : kNeg) : make_float2(xb, xl);
     if (lane == edge) {
       const unsigned long long v = pack(xl, slot_hi(0.0f, -1));
       if (OUT_GLOBAL) gstore(cx.gout + r, v);
@@ -292,12 +295,14 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
         const float d2 = xl - a2;
         const float l2 = log2_fast(1.0f + exp2_fast(-fabsf(d2)));
         const float h2 = __builtin_amdgcn_fmed3f(xl, a2, 3.0e38f);
-        const float nl = (h2 + el[i]) + l2;
+        // beta stores the sums before the emission: t for the blank, h2 + l2 for the label
+        const float pl = BETA ? h2 + l2 : 0.0f;
+        const float nl = BETA ? pl + el[i] : (h2 + el[i]) + l2;
         if (i + 1 < kK) n = dpp(lanef(hv, i + 1), nl);
         el[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(er, cx.eidx * 4, in_chunk(i) * Es * 4, 0));
         xb = nb;
         xl = nl;
-        const u32x2 st = BETA ? u32x2{__builtin_bit_cast(uint32_t, xl), __builtin_bit_cast(uint32_t, xb)}
+        const u32x2 st = BETA ? u32x2{__builtin_bit_cast(uint32_t, pl), __builtin_bit_cast(uint32_t, t)}
                               : u32x2{__builtin_bit_cast(uint32_t, xb), __builtin_bit_cast(uint32_t, xl)};
         __builtin_amdgcn_raw_buffer_store_b64(st, ab, lane * 8, in_chunk(i) * 512, 0);
         if (lane == edge) {

@@ -66,8 +66,8 @@ struct Layout {
 // consecutive sorted positions; each group runs its gather, recursions and rows on a stream of its
 // own, so the rows of short utterances overlap the recursions of long ones.  Three streams (the
 // caller's and two more) fit the hardware queues a process gets by default; group g ends where the
-// groups so far hold kGroupShare[K-1][g] of the rows, so that the group of the longest recursion
-// has few rows left to do after it.
+// groups so far hold a set share of the rows (schedule kernel), so that the group of the longest
+// recursion has few rows left to do after it.
 constexpr int kMaxGroups = 3;
 
 // the work of one group

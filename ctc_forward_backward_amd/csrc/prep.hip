@@ -288,8 +288,10 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
   }
   if (tid == 0) {
     // group g ends where the groups so far hold the share of the rows below (each group at least one
-    // utterance); its segments in sorted order, each utterance's producers first
-    const float share[kMaxGroups][kMaxGroups] = {{1.0f, 1.0f, 1.0f}, {0.15f, 1.0f, 1.0f}, {0.1f, 0.4f, 1.0f}};
+    // utterance); its segments in sorted order, each utterance's producers first.  With three
+    // groups: the longest recursions with few rows, then most of the long ones, then the short ones,
+    // whose rows finish while the long recursions still run
+    const float share[kMaxGroups][kMaxGroups] = {{1.0f, 1.0f, 1.0f}, {0.15f, 1.0f, 1.0f}, {0.1f, 0.7f, 1.0f}};
     int64_t total = 0;
     for (int i = 0; i < B; ++i) total += P.meta[sort ? sh[B + i] : i].T;
     int n = 0, pos = 0;

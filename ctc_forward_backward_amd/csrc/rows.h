@@ -10,7 +10,8 @@
 // column); rows owned by no utterance are zero; the row is stored in the dtype of the log probs.
 //
 // Design for gfx950:
-//   - posterior_row: one pass over the stored alpha and beta, 2^(alpha + beta - lp) taken relative
+//   - posterior_row: one pass over the stored alpha and beta (beta is stored without the frame's
+//     own emission, so alpha + beta is already alpha + beta - lp), 2^(alpha + beta) taken relative
 //     to the likelihood the alpha recursion reached (the block offsets of alpha and beta meet in
 //     that constant, so every term is at most about 1).  Blank states are summed in registers,
 //     label states added into an LDS array indexed by the rank of their class among the
@@ -59,8 +60,6 @@ __device__ __forceinline__ void posterior_row(const Layout& L, const Pointers& P
   auto offA = [&](int j) { return rowa < 0 ? 0 : P.sig[j * TT + rowa]; };
   auto offB = [&](int j) { return rowb < 0 ? 0 : P.sig[(Gm + j) * TT + rowb]; };
   const double lsh = P.lsh[b];
-  const float* Er = P.E + r * L.E_stride;
-  const float eb = Er[0];
   const int* dmap = P.dmap + (int64_t)b * (L.Umax + 1);
   // LDS operations of one wave complete in order: zeroing, atomics and reads need no barrier
   for (int i = lane; i <= U; i += 64) acc[i] = 0.0f;
@@ -70,13 +69,13 @@ __device__ __forceinline__ void posterior_row(const Layout& L, const Pointers& P
     // pair k = 64 j + lane: state 2k (blank) takes alpha at 2k and beta at 2k + 1; state 2k + 1
     // (label k + 1) alpha at 2k + 1 and beta at 2k + 2, which for lane 63 is the next block's first
     float2 a[kBlocks];
-    float b0[kBlocks], b1[kBlocks], el[kBlocks], c0[kBlocks], c1[kBlocks];
+    float b0[kBlocks], b1[kBlocks], c0[kBlocks], c1[kBlocks];
     int d1[kBlocks];
 #pragma unroll
     for (int u = 0; u < kBlocks; ++u) {
       const int j = j0 + u, k = 64 * j + lane;
       a[u] = make_float2(kNeg, kNeg);
-      b0[u] = b1[u] = el[u] = 0.0f;
+      b0[u] = b1[u] = 0.0f;
       c0[u] = c1[u] = 0.0f;
       d1[u] = 0;
       if (j < G) {
@@ -91,7 +90,6 @@ __device__ __forceinline__ void posterior_row(const Layout& L, const Pointers& P
         }
         if (k < U) {  // then for lane 63 the next block exists
           b1[u] = P.AB[lane < 63 ? rb + 2 * lane + 2 : rb + TT * 128];
-          el[u] = Er[k + 1];
           d1[u] = dmap[k + 1];
         }
       }
@@ -100,8 +98,8 @@ __device__ __forceinline__ void posterior_row(const Layout& L, const Pointers& P
     for (int u = 0; u < kBlocks; ++u) {
       const int k = 64 * (j0 + u) + lane;
       // each term is at most about 1; the clamp only guards the exponent against garbage
-      const float p0 = k <= U ? exp2_fast(fminf(a[u].x + b0[u] - eb + c0[u], 64.0f)) : 0.0f;
-      const float p1 = k < U ? exp2_fast(fminf(a[u].y + b1[u] - el[u] + c1[u], 64.0f)) : 0.0f;
+      const float p0 = k <= U ? exp2_fast(fminf(a[u].x + b0[u] + c0[u], 64.0f)) : 0.0f;
+      const float p1 = k < U ? exp2_fast(fminf(a[u].y + b1[u] + c1[u], 64.0f)) : 0.0f;
       z += p0 + p1;
       bsum += p0;
       if (k < U) atomicAdd(&acc[d1[u]], p1);

@@ -4,7 +4,8 @@
 loaded lazily so that the input generators in ``workloads`` import without the HIP library.
 """
 
-_API = ("packed_ctc_loss", "packed_ctc_reduce", "packed_ctc_workspace_size", "PackedCTCError", "library_path")
+_API = ("packed_ctc_loss", "packed_ctc_forward", "packed_ctc_backward", "ctc_loss", "PackedCTCLoss", "packed_ctc_reduce",
+        "packed_ctc_workspace_size", "PackedCTCError", "library_path")
 
 
 def __getattr__(name):

@@ -122,6 +122,39 @@ int packed_ctc_loss(const void* log_probs, int dtype, int64_t T_total, int64_t D
                     void* grad_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The same computation split at the autograd boundary ([PR] `_PackedCTCLoss.forward` stores alpha
+ * and the inputs; `_PackedCTCLoss.backward` runs beta and the gradient with the upstream
+ * `grad_output`).
+ *
+ * packed_ctc_forward: losses_out and reduced_out exactly as packed_ctc_loss with grad_out = NULL,
+ *   and the workspace left holding the recursions' state (alpha, beta, offsets, schedule) that
+ *   packed_ctc_backward reads.  Arguments as for packed_ctc_loss.
+ * packed_ctc_backward: grad_out (T_total, D) exactly as packed_ctc_loss would write it with the
+ *   given grad_scale and reduction (w_b = grad_scale[b] or 1, times 1/(B * max(U_b, 1)) for MEAN,
+ *   0 under zero_infinity for an infinite loss).  For autograd, grad_scale[b] is the upstream
+ *   gradient of loss b (NONE), or the upstream scalar for every b (SUM, MEAN).
+ *   Precondition: `workspace` holds the state of a packed_ctc_forward call on the same stream with
+ *   the same log_probs, sizes, index arrays, blank and max_target_length (>= 0 here: it must be the
+ *   bound the forward used; PCTC_ERR_ARG if negative), not reused by another call since.  The
+ *   workspace is read, and only its weight, class-map and row-sum regions are rewritten, so the
+ *   backward may be repeated with other grad_scale values.  zero_infinity and reduction may differ
+ *   from the forward's; they only set the weights.
+ * Error codes and alignment rules as for packed_ctc_loss.  Both calls are asynchronous on `stream`
+ *   and allocate nothing.
+ */
+int packed_ctc_forward(const void* log_probs, int dtype, int64_t T_total, int64_t D, const void* cu_seqlens,
+                       const void* lengths, int64_t B, const void* targets, int64_t target_width,
+                       const void* target_lengths, int index_flags, int64_t max_target_length, int blank,
+                       int zero_infinity, int reduction, float* losses_out, float* reduced_out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+int packed_ctc_backward(const void* log_probs, int dtype, int64_t T_total, int64_t D, const void* cu_seqlens,
+                        const void* lengths, int64_t B, const void* targets, int64_t target_width,
+                        const void* target_lengths, int index_flags, int64_t max_target_length, int blank,
+                        int zero_infinity, int reduction, const float* grad_scale, void* grad_out, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
  * Reduction of per-utterance losses ([PR] `ctc.py` `forward_packed`): SUM = sum of losses[b];
  * MEAN = mean over b of losses[b] / max(target_lengths[b], 1); B = 0 gives 0 (SUM) or NaN (MEAN).
  * Writes one float to *out (device).  NONE is PCTC_ERR_ARG.  Only the target-length bit of

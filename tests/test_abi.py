@@ -127,3 +127,45 @@ def test_binding_checks_without_gpu():
         api.packed_ctc_loss(torch.zeros(2, 5, 5), *args, blank=0)
     with pytest.raises(RuntimeError, match="GPU"):
         api.packed_ctc_loss(lp, *args, blank=0)
+
+
+def _split(which, **kw):
+    """packed_ctc_forward / packed_ctc_backward with dummy pointers; every case fails in the host checks."""
+    lib = api._load()
+    dummy = ctypes.c_void_p(0x1000)
+    a = dict(log_probs=dummy, dtype=0, T_total=10, D=5, cu=dummy, lengths=dummy, B=2, targets=dummy, W=3,
+             tl=dummy, flags=0, maxU=3, blank=0, zi=0, red=0, gs=None, losses=dummy, reduced=None, grad=dummy,
+             ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    head = (a["log_probs"], a["dtype"], a["T_total"], a["D"], a["cu"], a["lengths"], a["B"], a["targets"], a["W"],
+            a["tl"], a["flags"], a["maxU"], a["blank"], a["zi"], a["red"])
+    if which == "forward":
+        return lib.packed_ctc_forward(*head, a["losses"], a["reduced"], a["ws"], a["ws_bytes"], a["stream"])
+    return lib.packed_ctc_backward(*head, a["gs"], a["grad"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("which,kw,code,needle", [
+    ("forward", dict(dtype=3), api.ERR_DTYPE, "float32"),
+    ("forward", dict(blank=7), api.ERR_BLANK, "blank"),
+    ("forward", dict(losses=None), api.ERR_ARG, "required"),
+    ("forward", dict(ws=None, ws_bytes=0), api.ERR_WORKSPACE, "workspace"),
+    ("backward", dict(maxU=-1), api.ERR_ARG, "max_target_length"),
+    ("backward", dict(grad=None), api.ERR_ARG, "grad_out"),
+    ("backward", dict(grad=ctypes.c_void_p(0x1004)), api.ERR_ARG, "aligned"),
+    ("backward", dict(red=5), api.ERR_ARG, "reduction"),
+    ("backward", dict(ws=ctypes.c_void_p(0x1000), ws_bytes=16), api.ERR_WORKSPACE, "workspace"),
+])
+def test_split_entry_points_host_checks(which, kw, code, needle):
+    rc = _split(which, **kw)
+    assert rc == code
+    assert needle in api._load().packed_ctc_last_error().decode()
+
+
+def test_autograd_binding_checks_without_gpu():
+    lp = torch.zeros(10, 5, requires_grad=True)
+    args = (torch.tensor([0, 6, 10], dtype=torch.int32), torch.tensor([6, 4]), torch.zeros(2, 2, dtype=torch.long),
+            torch.tensor([1, 2]))
+    with pytest.raises(RuntimeError, match="GPU"):
+        api.ctc_loss(lp, *args, blank=0)
+    with pytest.raises(ValueError, match="shape"):
+        api.ctc_loss(torch.zeros(2, 5, 5, requires_grad=True), *args, blank=0)

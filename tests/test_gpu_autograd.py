@@ -1,0 +1,214 @@
+"""The split entry points (packed_ctc_forward / packed_ctc_backward), the autograd binding and graph
+capture, on the GPU, through the C ABI.
+
+- The split call gives the fused call's losses and gradient (the same kernels; float32 workloads,
+  within 1e-6, since class sums are accumulated with LDS atomics in no fixed order).
+- The backward with upstream weights matches the float64 oracle with those weights as grad_scale,
+  at the parity tolerances (losses 1e-4 / 2e-3 relative, gradients 1e-4 / 2e-3 absolute for
+  float32 / 16-bit inputs; for the gradient, beyond half an ulp of the stored dtype at the exact
+  value, and times max(1, |w_b|) on the rows of utterance b: the bar is set for unit weights, and
+  an upstream weight scales the gradient and its error, while the stored value's own rounding
+  grows with its magnitude);
+  a second backward on the same forward state matches as well.
+- Autograd (`ctc_loss` + `.backward`) for none / sum / mean matches the oracle.
+- A captured graph of the fused call and one of the autograd forward + backward, with the target
+  bound set to the targets width (no host read), replayed several times on fresh inputs with eager
+  work between replays: every replay matches an eager call on the same inputs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from ctc_forward_backward_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: (1e-4, 1e-4), torch.bfloat16: (2e-3, 2e-3), torch.float16: (2e-3, 2e-3)}
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from ctc_forward_backward_amd import api as _api
+
+    _api._load()
+    return _api
+
+
+def _dev_args(b):
+    dev = torch.device("cuda:0")
+    return (b.cu_seqlens.to(dev), b.lengths.to(dev), b.targets.to(dev), b.target_lengths.to(dev))
+
+
+def _row_scale(b, gs):
+    """Per-row tolerance factor max(1, |w_b|): the bar is for unit weights, and an upstream weight w
+    scales the gradient, and the rounding of its stored 16-bit value, by |w|."""
+    f = np.ones(int(b.T_total))
+    cu, ln = b.cu_seqlens.numpy(), b.lengths.numpy()
+    for i in range(int(b.B)):
+        f[int(cu[i]):int(cu[i]) + int(ln[i])] = max(1.0, abs(float(gs[i])))
+    return f
+
+
+def _half_ulp(x, dtype):
+    """Half a unit in the last place of `dtype` at |x| (the most that rounding the exact value to the
+    stored dtype moves it): 2^(e-8) for bfloat16, 2^(e-11) for float16 with |x| in [2^e, 2^(e+1))."""
+    bits = {torch.bfloat16: 8, torch.float16: 11, torch.float32: 24}[dtype]
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, np.exp2(e - bits), 0.0)
+
+
+def _check_oracle(losses, grad, ref, dtype, label, row_scale=None):
+    lrt, gat = TOL[dtype]
+    loss = losses.detach().cpu().double().numpy()
+    rloss = ref["loss"]
+    assert np.array_equal(np.isinf(loss), np.isinf(rloss)), label
+    fin = ~np.isinf(rloss)
+    np.testing.assert_allclose(loss[fin], rloss[fin], rtol=lrt, atol=1e-5, err_msg=label)
+    if grad is not None:
+        g = grad.detach().cpu().double().numpy()
+        rg = ref["grad"]
+        nan_ref = np.isnan(rg)
+        assert np.array_equal(np.isnan(g), nan_ref), label
+        scale = np.ones(g.shape[0]) if row_scale is None else row_scale
+        rgf = np.nan_to_num(rg)
+        # the bar scaled by max(1, |w_b|), beyond the rounding of the exact value to the stored dtype
+        err = (np.maximum(np.abs(np.nan_to_num(g) - rgf) - _half_ulp(rgf, dtype), 0.0) / scale[:, None])[~nan_ref]
+        worst = float(err.max()) if err.size else 0.0
+        _say(f"  {label}: max (|grad err| - half ulp) / max(1, |w|) = {worst:.3e} (tol {gat})")
+        assert worst <= gat, f"{label}: gradient error {worst} > {gat}"
+
+
+@pytest.mark.parametrize("name", ["small", "char_level"])
+def test_split_matches_fused(api, name):
+    _say(f"[gpu autograd] split vs fused, workload {name}")
+    b = W.make_workload(name)
+    lp = b.log_probs.to("cuda:0")
+    args = _dev_args(b)
+    kw = dict(blank=b.blank, zero_infinity=b.zero_infinity, reduction=b.reduction)
+    l1, r1, g1 = api.packed_ctc_loss(lp, *args, **kw)
+    l2, r2, state = api.packed_ctc_forward(lp, *args, **kw)
+    g2 = api.packed_ctc_backward(state, zero_infinity=b.zero_infinity)
+    torch.cuda.synchronize()
+    assert api.last_call_status() == 0
+    assert torch.allclose(l1, l2, rtol=1e-6, atol=0), name
+    assert torch.allclose(r1, r2, rtol=1e-6, atol=0), name
+    assert float((g1.double() - g2.double()).abs().max()) <= 1e-6, name
+
+
+@pytest.mark.parametrize("name", ["tiny", "asr_bpe", "large_vocab"])
+def test_backward_weights_vs_oracle(api, oracle_mod, name):
+    _say(f"[gpu autograd] backward with upstream weights, workload {name}")
+    b = W.make_workload(name)
+    lp = b.log_probs.to("cuda:0")
+    losses, _, state = api.packed_ctc_forward(lp, *_dev_args(b), blank=b.blank, zero_infinity=b.zero_infinity,
+                                              reduction="none")
+    rng = np.random.default_rng(21)
+    for k in range(2):  # the same forward state serves two backward calls
+        gs = rng.normal(0.0, 1.0, size=b.B).astype(np.float32)
+        gs[0] = 0.0
+        grad = api.packed_ctc_backward(state, torch.from_numpy(gs), zero_infinity=b.zero_infinity, reduction="none")
+        torch.cuda.synchronize()
+        ref = oracle_mod.ctc_batch(b, reduction="none", grad_scale=gs.astype(np.float64))
+        _check_oracle(losses, grad, ref, b.log_probs.dtype, f"{name}/backward {k}", _row_scale(b, gs))
+    assert api.last_call_status() == 0
+
+
+@pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
+def test_autograd_vs_oracle(api, oracle_mod, reduction):
+    _say(f"[gpu autograd] ctc_loss.backward, reduction {reduction}")
+    b = W.make_workload("small")
+    lp = b.log_probs.to("cuda:0").requires_grad_(True)
+    out = api.ctc_loss(lp, *_dev_args(b), blank=b.blank, zero_infinity=b.zero_infinity, reduction=reduction)
+    if reduction == "none":
+        g = torch.linspace(-1.5, 2.0, b.B, dtype=torch.float32, device="cuda:0")
+        out.backward(g)
+        gs = g.cpu().double().numpy()
+    else:
+        assert out.ndim == 0
+        out.backward(torch.tensor(0.75, device="cuda:0"))
+        gs = np.full(b.B, 0.75)
+    torch.cuda.synchronize()
+    ref = oracle_mod.ctc_batch(b, reduction=reduction, grad_scale=gs)
+    losses = out if reduction == "none" else torch.from_numpy(ref["loss"])  # scalar checked below
+    _check_oracle(losses, lp.grad, ref, b.log_probs.dtype, f"autograd/{reduction}", _row_scale(b, gs))
+    if reduction != "none":
+        np.testing.assert_allclose(float(out.detach().cpu()), ref["reduced"], rtol=1e-4)
+    assert lp.grad.dtype == lp.dtype
+
+
+def _fresh_lp(b, k):
+    rng = np.random.default_rng(100 + k)
+    logits = rng.normal(0.0, 2.0, size=tuple(b.log_probs.shape))
+    lp = logits - np.log(np.exp(logits - logits.max(1, keepdims=True)).sum(1, keepdims=True)) - logits.max(1, keepdims=True)
+    return torch.from_numpy(lp).to(b.log_probs.dtype)
+
+
+def test_graph_capture_fused_call(api):
+    _say("[gpu autograd] graph capture of the fused call")
+    b = W.make_workload("small")
+    dev = torch.device("cuda:0")
+    args = _dev_args(b)
+    Wd = int(b.targets.shape[1])
+    kw = dict(blank=b.blank, zero_infinity=b.zero_infinity, reduction=b.reduction, max_target_length=Wd)
+    lp_static = b.log_probs.to(dev).clone()
+    api.packed_ctc_loss(lp_static, *args, **kw)  # eager first: the library's group streams exist
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        losses, reduced, grad = api.packed_ctc_loss(lp_static, *args, **kw)
+    for k in range(3):
+        fresh = _fresh_lp(b, k).to(dev)
+        lp_static.copy_(fresh)
+        graph.replay()
+        torch.cuda.synchronize()
+        el, er, eg = api.packed_ctc_loss(fresh, *args, **kw)  # eager work between replays
+        torch.cuda.synchronize()
+        assert api.last_call_status() == 0
+        assert torch.allclose(losses, el, rtol=1e-6, atol=0), k
+        assert torch.allclose(reduced, er, rtol=1e-6, atol=0), k
+        assert float((grad.double() - eg.double()).abs().max()) <= 1e-6, k
+        _say(f"  replay {k}: matches the eager call")
+
+
+def test_graph_capture_autograd(api):
+    _say("[gpu autograd] graph capture of ctc_loss forward + backward")
+    b = W.make_workload("small")
+    dev = torch.device("cuda:0")
+    args = _dev_args(b)
+    Wd = int(b.targets.shape[1])
+    kw = dict(blank=b.blank, zero_infinity=b.zero_infinity, reduction="mean", max_target_length=Wd)
+    lp_static = b.log_probs.to(dev).clone().requires_grad_(True)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):  # warm-up outside the capture, as torch asks
+        for _ in range(2):
+            lp_static.grad = None
+            api.ctc_loss(lp_static, *args, **kw).backward()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    lp_static.grad = None
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = api.ctc_loss(lp_static, *args, **kw)
+        out.backward()
+    for k in range(3):
+        fresh = _fresh_lp(b, 10 + k).to(dev)
+        with torch.no_grad():
+            lp_static.copy_(fresh)
+        graph.replay()
+        torch.cuda.synchronize()
+        ref_lp = fresh.clone().requires_grad_(True)
+        ref_out = api.ctc_loss(ref_lp, *args, **kw)  # eager work between replays
+        ref_out.backward()
+        torch.cuda.synchronize()
+        assert torch.allclose(out.detach(), ref_out.detach(), rtol=1e-6, atol=0), k
+        assert float((lp_static.grad.double() - ref_lp.grad.double()).abs().max()) <= 1e-6, k
+        _say(f"  replay {k}: matches the eager forward + backward")

@@ -259,13 +259,17 @@ __global__ void __launch_bounds__(256) reduce_kernel(const float* losses, const 
 // which sits earlier in the queue, so segments claimed in queue order can always finish.
 // Frameless utterances get their loss here.
 __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, int sort, int groups) {
-  extern __shared__ int sh[];  // sort ? [T (B) | order (B)] : unused
+  extern __shared__ int sh[];  // sort ? [T (B) | order (B) | U (B)] : unused
   const int B = static_cast<int>(L.B);
   const int tid = threadIdx.x, nt = blockDim.x;
   if (sort) {
     int* sT = sh;
     int* order = sh + B;
-    for (int b = tid; b < B; b += nt) sT[b] = P.meta[b].T;
+    for (int b = tid; b < B; b += nt) {
+      const Meta m = P.meta[b];
+      sT[b] = m.T;
+      sh[2 * B + b] = m.U;
+    }
     __syncthreads();
     for (int b = tid; b < B; b += nt) {
       const int Tb = sT[b];
@@ -289,11 +293,16 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
   if (tid == 0) {
     // group g ends where the groups so far hold the share of the rows below (each group at least one
     // utterance); its segments in sorted order, each utterance's producers first.  With three
-    // groups: the longest recursions with few rows, then most of the long ones, then the short ones,
-    // whose rows finish while the long recursions still run
-    const float share[kMaxGroups][kMaxGroups] = {{1.0f, 1.0f, 1.0f}, {0.15f, 1.0f, 1.0f}, {0.1f, 0.7f, 1.0f}};
+    // groups (cut points measured on uniformly spread lengths): the longest recursions with about
+    // half the rows on the caller's stream, then the middle, then the short ones, whose gathers,
+    // recursions and rows all finish under the long recursions
+    const float share[kMaxGroups][kMaxGroups] = {{1.0f, 1.0f, 1.0f}, {0.15f, 1.0f, 1.0f}, {0.45f, 0.75f, 1.0f}};
+    // frame and label counts from LDS when sorted (a serial walk over global memory would wait on
+    // every load)
+    auto Tat = [&](int b) { return sort ? sh[b] : P.meta[b].T; };
+    auto Uat = [&](int b) { return sort ? sh[2 * B + b] : P.meta[b].U; };
     int64_t total = 0;
-    for (int i = 0; i < B; ++i) total += P.meta[sort ? sh[B + i] : i].T;
+    for (int i = 0; i < B; ++i) total += Tat(sort ? sh[B + i] : i);
     int n = 0, pos = 0;
     int64_t done = 0;
     for (int g = 0; g < kMaxGroups; ++g) {
@@ -304,7 +313,7 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
         int p1 = p0;
         const int keep = groups - 1 - g;  // utterances to leave for the groups after this one
         do {
-          done += P.meta[sort ? sh[B + p1] : p1].T;
+          done += Tat(sort ? sh[B + p1] : p1);
           ++p1;
         } while (p1 < B - keep && (done < goal || g == groups - 1));
         q.itemoff = n;
@@ -313,12 +322,12 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
         int rows = 0;
         for (int i = p0; i < p1; ++i) {
           const int b = sort ? sh[B + i] : i;
-          const Meta m = P.meta[b];
+          const int Tb = Tat(b), Ub = Uat(b);
           P.cum[i] = rows;
-          rows += m.T;
-          if (m.T == 0) continue;
+          rows += Tb;
+          if (Tb == 0) continue;
           // segments of kSegWaves 64-pair blocks
-          const int nseg = (((m.U + 1 + 63) >> 6) + kSegWaves - 1) / kSegWaves;
+          const int nseg = (((Ub + 1 + 63) >> 6) + kSegWaves - 1) / kSegWaves;
           for (int j = 0; j < nseg; ++j) {
             P.items[n++] = ((2 * b) << 12) | j;
             P.items[n++] = ((2 * b + 1) << 12) | (nseg - 1 - j);
@@ -392,7 +401,7 @@ hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P,
   const int64_t words = 2 * 2 * L.Gmax * L.T_total;
   if (words > 0) fill_i32_kernel<<<grid_for(words, 256), 256, 0, s>>>(reinterpret_cast<int*>(P.ring), words, 0);
   const int sort = L.B <= 8192 ? 1 : 0;
-  const size_t lds = sort ? 2 * sizeof(int) * (size_t)L.B : 0;
+  const size_t lds = sort ? 3 * sizeof(int) * (size_t)L.B : 0;
   if (lds > 48 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&schedule_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));

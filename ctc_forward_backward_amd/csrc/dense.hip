@@ -103,6 +103,7 @@ hipError_t launch_dense(const Inputs& in, const Layout& L, const Pointers& P, vo
     return hipGetLastError();
   };
   if (in.dtype == kF32) return launch(&dense_kernel<kF32>);
+  if (in.dtype == kF64) return launch(&dense_kernel<kF64>);
   if (in.dtype == kF16) return launch(&dense_kernel<kF16>);
   return launch(&dense_kernel<kBF16>);
 }
@@ -114,6 +115,7 @@ hipError_t launch_gaps(const Inputs& in, const Layout& L, const Pointers& P, voi
   const int grid = static_cast<int>(((L.T_total + rpw - 1) / rpw + 3) / 4);
   const int rows = static_cast<int>(rpw);
   if (in.dtype == kF32) gap_kernel<kF32><<<grid, 256, 0, s>>>(L, P, grad_out, rows);
+  else if (in.dtype == kF64) gap_kernel<kF64><<<grid, 256, 0, s>>>(L, P, grad_out, rows);
   else if (in.dtype == kF16) gap_kernel<kF16><<<grid, 256, 0, s>>>(L, P, grad_out, rows);
   else gap_kernel<kBF16><<<grid, 256, 0, s>>>(L, P, grad_out, rows);
   return hipGetLastError();

@@ -25,7 +25,7 @@ constexpr double kLn2 = 0.6931471805599453;
 constexpr int kMaxTargetLength = 8191;  // S = 2U+1 <= 16383 states per utterance
 constexpr int kMaxClasses = 32768;      // per-class posterior accumulator in LDS (128 KB)
 
-enum Dtype { kF32 = 0, kBF16 = 1, kF16 = 2 };
+enum Dtype { kF32 = 0, kBF16 = 1, kF16 = 2, kF64 = 3 };
 
 struct Meta {
   int start;  // first row
@@ -142,6 +142,7 @@ __device__ __forceinline__ float lse3(float a, float b, float c) {
 
 __device__ __forceinline__ float load_lp(const void* p, int dtype, int64_t i) {
   if (dtype == kF32) return static_cast<const float*>(p)[i];
+  if (dtype == kF64) return static_cast<float>(static_cast<const double*>(p)[i]);
   if (dtype == kF16) return static_cast<float>(static_cast<const _Float16*>(p)[i]);
   const uint32_t bits = static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16;
   return __builtin_bit_cast(float, bits);
@@ -156,6 +157,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
 __device__ __forceinline__ void store_grad(void* p, int dtype, int64_t i, float v) {
   if (dtype == kF32) {
     static_cast<float*>(p)[i] = v;
+  } else if (dtype == kF64) {
+    static_cast<double*>(p)[i] = static_cast<double>(v);
   } else if (dtype == kF16) {
     static_cast<_Float16*>(p)[i] = static_cast<_Float16>(v);
   } else {
@@ -201,18 +204,23 @@ __device__ __forceinline__ void wave_share(const Pointers& P, int g, int64_t wid
 }
 
 // ---- 8-element chunks of a (T_total, D) log-prob / gradient buffer ----------------------------
-// Chunk q holds flat elements [8q, 8q+8): 16 aligned bytes for 16-bit dtypes, 32 for float32.
+// Chunk q holds flat elements [8q, 8q+8): 16 aligned bytes for 16-bit dtypes, 32 for float32, 64 for
+// float64 (read into float32 arithmetic; the gradient goes back as float64).
 
 // Raw bytes of one chunk, held while its load is in flight.
 template <int DT>
 struct Raw8 {
-  uint4 u[DT == kF32 ? 2 : 1];
+  uint4 u[DT == kF64 ? 4 : (DT == kF32 ? 2 : 1)];
 };
 
 template <int DT>
 __device__ __forceinline__ Raw8<DT> ld8(const void* base, int64_t q) {
   Raw8<DT> r;
-  if constexpr (DT == kF32) {
+  if constexpr (DT == kF64) {
+    const uint4* p = static_cast<const uint4*>(base) + 4 * q;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.u[i] = p[i];
+  } else if constexpr (DT == kF32) {
     const uint4* p = static_cast<const uint4*>(base) + 2 * q;
     r.u[0] = p[0];
     r.u[1] = p[1];
@@ -224,7 +232,13 @@ __device__ __forceinline__ Raw8<DT> ld8(const void* base, int64_t q) {
 
 template <int DT>
 __device__ __forceinline__ void unpack8(const Raw8<DT>& r, float v[8]) {
-  if constexpr (DT == kF32) {
+  if constexpr (DT == kF64) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = static_cast<float>(__builtin_bit_cast(double, (uint64_t)r.u[i].x | ((uint64_t)r.u[i].y << 32)));
+      v[2 * i + 1] = static_cast<float>(__builtin_bit_cast(double, (uint64_t)r.u[i].z | ((uint64_t)r.u[i].w << 32)));
+    }
+  } else if constexpr (DT == kF32) {
     const uint32_t w[8] = {r.u[0].x, r.u[0].y, r.u[0].z, r.u[0].w, r.u[1].x, r.u[1].y, r.u[1].z, r.u[1].w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = __builtin_bit_cast(float, w[i]);
@@ -245,7 +259,16 @@ __device__ __forceinline__ void unpack8(const Raw8<DT>& r, float v[8]) {
 
 template <int DT>
 __device__ __forceinline__ void store8(void* base, int64_t q, const float v[8]) {
-  if constexpr (DT == kF32) {
+  if constexpr (DT == kF64) {
+    uint4* p = static_cast<uint4*>(base) + 4 * q;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t a = __builtin_bit_cast(uint64_t, static_cast<double>(v[2 * i]));
+      const uint64_t b = __builtin_bit_cast(uint64_t, static_cast<double>(v[2 * i + 1]));
+      p[i] = make_uint4(static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32), static_cast<uint32_t>(b),
+                        static_cast<uint32_t>(b >> 32));
+    }
+  } else if constexpr (DT == kF32) {
     float4* p = static_cast<float4*>(base) + 2 * q;
     p[0] = make_float4(v[0], v[1], v[2], v[3]);
     p[1] = make_float4(v[4], v[5], v[6], v[7]);

@@ -79,6 +79,7 @@ constexpr int kGLab = 8;  // label columns per lane held in registers
 template <int DT>
 __device__ __forceinline__ float ld1(const void* p, int64_t i) {
   if constexpr (DT == kF32) return static_cast<const float*>(p)[i];
+  else if constexpr (DT == kF64) return static_cast<float>(static_cast<const double*>(p)[i]);
   else if constexpr (DT == kF16) return static_cast<float>(static_cast<const _Float16*>(p)[i]);
   else return __builtin_bit_cast(float, static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
 }
@@ -372,6 +373,7 @@ hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, i
   const int grid = 8 * (cus > 0 ? cus : 256);
   const size_t lds = kRowKernelLds;
   if (in.dtype == kF32) gather_kernel<kF32><<<grid, 256, lds, s>>>(in, L, P, group);
+  else if (in.dtype == kF64) gather_kernel<kF64><<<grid, 256, lds, s>>>(in, L, P, group);
   else if (in.dtype == kF16) gather_kernel<kF16><<<grid, 256, lds, s>>>(in, L, P, group);
   else gather_kernel<kBF16><<<grid, 256, lds, s>>>(in, L, P, group);
   return hipGetLastError();

@@ -37,7 +37,7 @@ constexpr int kPost = 8;    // compact class sums per lane held in registers (U+
 
 // aligned 8-element row chunks per lane loaded at once (the whole row for D <= 8192 at 2 bytes)
 template <int DT>
-constexpr int row_batch() { return DT == kF32 ? 8 : 16; }
+constexpr int row_batch() { return DT == kF64 ? 4 : (DT == kF32 ? 8 : 16); }
 
 // a row gets a gradient from its utterance only if the utterance has a non-zero weight and an
 // alignment (a NaN input makes the loss NaN, which also fails the test)

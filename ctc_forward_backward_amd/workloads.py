@@ -25,7 +25,7 @@ import torch
 
 __all__ = ["PackedBatch", "WORKLOADS", "make_workload", "make_batch", "log_softmax_rounded"]
 
-_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16, "f64": torch.float64}
 
 
 @dataclass

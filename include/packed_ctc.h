@@ -33,11 +33,13 @@
 extern "C" {
 #endif
 
-/* log_probs / grad dtypes ([PR] `PACKED_CTC_LOSS_DTYPES`: float32, bfloat16, float16; float64 is
- * rejected by the kernel) */
+/* log_probs / grad dtypes ([PR] `PACKED_CTC_LOSS_DTYPES`: float32, bfloat16, float16; the page sends
+ * float64 to the padded path).  F64 is this library's own addition: float64 log probs are read as
+ * float64 and carried in float32 arithmetic like the others; the gradient is written as float64. */
 #define PCTC_DTYPE_F32 0
 #define PCTC_DTYPE_BF16 1
 #define PCTC_DTYPE_F16 2
+#define PCTC_DTYPE_F64 3
 
 /* index_flags: a set bit makes that array int64, a clear bit int32 */
 #define PCTC_I64_CU_SEQLENS 1
@@ -54,7 +56,7 @@ extern "C" {
 /* error codes, one per failure class of [PR] `packed_ctc_loss` argument checks */
 #define PCTC_OK 0
 #define PCTC_ERR_SHAPE 1              /* a size is negative or inconsistent (the page's ValueError on shapes) */
-#define PCTC_ERR_DTYPE 2              /* log_probs dtype not F32/BF16/F16 (the page's TypeError) */
+#define PCTC_ERR_DTYPE 2              /* log_probs dtype not F32/BF16/F16/F64 (the page's TypeError) */
 #define PCTC_ERR_BLANK 3              /* blank outside [0, D) */
 #define PCTC_ERR_NEG_TARGET_LENGTH 4  /* a negative target length (checked on the host read) */
 #define PCTC_ERR_TARGET_LENGTH_WIDTH 5/* a target length beyond target_width (checked on the host read) */

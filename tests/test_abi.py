@@ -85,7 +85,7 @@ def _call(**kw):
 @pytest.mark.parametrize("kw,code,needle", [
     (dict(T_total=-1), api.ERR_SHAPE, "shape"),
     (dict(D=-3), api.ERR_SHAPE, "shape"),
-    (dict(dtype=3), api.ERR_DTYPE, "float32"),
+    (dict(dtype=4), api.ERR_DTYPE, "float32"),
     (dict(dtype=7), api.ERR_DTYPE, "float32"),
     (dict(B=-1), api.ERR_SHAPE, "batch"),
     (dict(W=-1), api.ERR_SHAPE, "width"),
@@ -145,7 +145,7 @@ def _split(which, **kw):
 
 
 @pytest.mark.parametrize("which,kw,code,needle", [
-    ("forward", dict(dtype=3), api.ERR_DTYPE, "float32"),
+    ("forward", dict(dtype=4), api.ERR_DTYPE, "float32"),
     ("forward", dict(blank=7), api.ERR_BLANK, "blank"),
     ("forward", dict(losses=None), api.ERR_ARG, "required"),
     ("forward", dict(ws=None, ws_bytes=0), api.ERR_WORKSPACE, "workspace"),

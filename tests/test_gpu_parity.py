@@ -1,6 +1,7 @@
 """HIP path vs the float64 oracle, element by element, through the C ABI.
 
-Tolerances: losses within 1e-4 relative for float32 inputs and 2e-3 for bfloat16 / float16 inputs;
+Tolerances: losses within 1e-4 relative for float32 (and float64, carried in float32 arithmetic)
+inputs and 2e-3 for bfloat16 / float16 inputs;
 gradients within 1e-4 / 2e-3 absolute (the gradient is stored in the input dtype, so for bfloat16 /
 float16 the rounding of the stored value is part of the budget).  Several results are correct where
 the method sums repeated labels in any order; the comparison is tolerance-based throughout.
@@ -16,7 +17,8 @@ from ctc_forward_backward_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-TOL = {torch.float32: (1e-4, 1e-4), torch.bfloat16: (2e-3, 2e-3), torch.float16: (2e-3, 2e-3)}
+TOL = {torch.float32: (1e-4, 1e-4), torch.float64: (1e-4, 1e-4), torch.bfloat16: (2e-3, 2e-3),
+       torch.float16: (2e-3, 2e-3)}
 
 
 def _say(*a):
@@ -209,8 +211,8 @@ def test_host_read_errors(api):
         api.packed_ctc_loss(*args, torch.tensor([3, -1, 2, 2], device=dev), blank=0)
     with pytest.raises(ValueError, match="targets width"):
         api.packed_ctc_loss(*args, b.target_lengths.to(dev) + 100, blank=0)
-    with pytest.raises(TypeError, match="float32"):
-        api.packed_ctc_loss(b.log_probs.double().to(dev), *args[1:], b.target_lengths.to(dev), blank=0)
+    with pytest.raises(TypeError, match="float32"):  # float64 is accepted (its own path); integers are not
+        api.packed_ctc_loss(b.log_probs.to(torch.int32).to(dev), *args[1:], b.target_lengths.to(dev), blank=0)
     with pytest.raises(ValueError, match="blank"):
         api.packed_ctc_loss(*args, b.target_lengths.to(dev), blank=16)
 
@@ -243,3 +245,19 @@ def test_repeatable_within_tolerance(api):
     c = run_gpu(api, b)
     np.testing.assert_allclose(a["loss"], c["loss"], rtol=1e-6)
     np.testing.assert_allclose(np.nan_to_num(a["grad"]), np.nan_to_num(c["grad"]), atol=2e-3)
+
+
+@pytest.mark.parametrize("reduction", ["none", "mean"])
+def test_float64_inputs(api, oracle_mod, reduction):
+    """float64 log probs, read as float64, carried in float32 arithmetic, gradient written as float64:
+    the float32 tolerances; several tiles of a 1025-class row and a ragged tail."""
+    _say(f"[gpu parity] float64 inputs, reduction {reduction}")
+    rng = np.random.default_rng(31)
+    lengths = [int(x) for x in rng.integers(1, 400, size=11)] + [0, 3]
+    tl = [int(rng.integers(0, max(1, T // 3) + 1)) for T in lengths]
+    tl[-2] = 0
+    targets = [[int(x) for x in rng.integers(1, 1025, size=u)] for u in tl]
+    b = W.make_batch(lengths, targets, 1025, seed=9, sigma=3.0, dtype="f64", reduction=reduction)
+    got = run_gpu(api, b)
+    assert got["grad_dtype"] == torch.float64
+    compare(got, oracle_mod.ctc_batch(b), torch.float64, f"f64/{reduction}")

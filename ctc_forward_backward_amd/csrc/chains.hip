@@ -185,6 +185,7 @@ struct Ctx {
   int* prog_self;
   int* sig;                 // this block's offset per chunk, at the row of the chunk's first frame
   float* ab;                // this block's 128 states per row (row 0)
+  bool store;               // keep the states and offsets (false: loss only, nothing is written)
   int* err;
   const Inputs* in;
   int64_t B;
@@ -219,8 +220,9 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
     xl = (first && cx.vl) ? el : kNeg;
     // beta is stored without the frame's own emission (the empty sum 0 at its start states), so that
     // alpha + stored beta is the posterior's exponent with no emission to take out
-    *reinterpret_cast<float2*>(cx.ab + r * 128 + 2 * lane) =
-        BETA ? make_float2((first && cx.vl) ? 0.0f : kNeg, first ? 0.0f : kNeg) : make_float2(xb, xl);
+    if (cx.store)
+      *reinterpret_cast<float2*>(cx.ab + r * 128 + 2 * lane) =
+          BETA ? make_float2((first && cx.vl) ? 0.0f : kNeg, first ? 0.0f : kNeg) : make_float2(xb, xl);
     if (lane == edge) {
       const unsigned long long v = pack(xl, slot_hi(0.0f, -1));
       if (OUT_GLOBAL) gstore(cx.gout + r, v);
@@ -261,7 +263,7 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
       const bool check_cons = !OUT_GLOBAL && cx.lout_live && c >= kR / kK - 1;
       const int cons = check_cons ? __hip_atomic_load(cx.prog_cons, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0;
       const float ebn = P.Eb[row(1 + (int64_t)(c + 1) * kK + lk)];
-      cx.sig[row(1 + (int64_t)c * kK)] = static_cast<int>(off);
+      if (cx.store) cx.sig[row(1 + (int64_t)c * kK)] = static_cast<int>(off);
       if (IN_GLOBAL) {
         if (__ballot(need && !global_ok(raw))) raw = wait_global(cx.gin + row(min(c * kK + lk, nsteps)), raw, need, err);
         hraw = cx.no_in ? none : gload(cx.gin + row(min((c + 1) * kK + lk, nsteps)));
@@ -272,8 +274,9 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
       // the consumer of this block's LDS ring must have taken the chunk whose slots this one reuses
       if (check_cons && cons < c - (kR / kK - 1)) wait_progress(cx.prog_cons, c - (kR / kK - 1), err);
       const float hv = slot_value(raw, off);
-      const __amdgpu_buffer_rsrc_t ab = __builtin_amdgcn_make_buffer_rsrc(cx.ab + chunk_lo(c) * 128, 0, kK * 512,
-                                                                          kRsrcWord3);
+      // loss only: a resource of no bytes, so the hardware discards the per-frame stores (range check)
+      const __amdgpu_buffer_rsrc_t ab = __builtin_amdgcn_make_buffer_rsrc(cx.ab + chunk_lo(c) * 128, 0,
+                                                                          cx.store ? kK * 512 : 0, kRsrcWord3);
       const __amdgpu_buffer_rsrc_t er = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float*>(P.E + chunk_lo(c + 1) * Es), 0, static_cast<int>(kK * Es * 4), kRsrcWord3);
       const uint32_t hi = slot_hi(off, c);
@@ -366,7 +369,7 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
 
 // One block (this wave) of segment `seg` of chain (utterance, direction).
 __device__ __forceinline__ void run_wave(const Inputs& in, const Layout& L, const Pointers& P, Shared& sh, int chain,
-                                         int seg, int w, int lane) {
+                                         int seg, int w, int lane, bool store) {
   Ctx cx;
   cx.b = chain >> 1;
   const bool beta = chain & 1;
@@ -406,6 +409,7 @@ __device__ __forceinline__ void run_wave(const Inputs& in, const Layout& L, cons
   cx.prog_self = &sh.prog[w];
   cx.sig = P.sig + (dir * Gm + j) * TT;
   cx.ab = P.AB + (dir * Gm + j) * TT * 128;
+  cx.store = store;
   cx.err = &P.ctl->err;
   cx.in = &in;
   cx.B = L.B;
@@ -431,7 +435,7 @@ __device__ __forceinline__ void run_wave(const Inputs& in, const Layout& L, cons
   __builtin_amdgcn_s_setprio(0);
 }
 
-__global__ void __launch_bounds__(kThreads, 1) chain_workers(Inputs in, Layout L, Pointers P, int group) {
+__global__ void __launch_bounds__(kThreads, 1) chain_workers(Inputs in, Layout L, Pointers P, int group, int store) {
   __shared__ Shared sh;
   // the wave index and the claimed item are wave-uniform: say so, so that every address derived
   // from them stays in scalar registers
@@ -448,7 +452,7 @@ __global__ void __launch_bounds__(kThreads, 1) chain_workers(Inputs in, Layout L
     const int idx = __builtin_amdgcn_readfirstlane(sh.item);
     if (idx >= qlen) break;
     const int item = __builtin_amdgcn_readfirstlane(items[idx]);
-    run_wave(in, L, P, sh, item >> 12, item & 4095, w, lane);
+    run_wave(in, L, P, sh, item >> 12, item & 4095, w, lane, store != 0);
     __syncthreads();
   }
 }
@@ -462,7 +466,7 @@ constexpr size_t kChainReserve = 152 * 1024;
 static_assert(kChainReserve + sizeof(Shared) <= 160 * 1024 && kChainReserve + sizeof(Shared) + kRowKernelLds > 160 * 1024,
               "one recursion workgroup per compute unit, alone");
 
-hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s) {
+hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, int group, bool store, hipStream_t s) {
   if (L.B == 0 || L.T_total == 0) return hipGetLastError();
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -472,7 +476,7 @@ hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, i
                             static_cast<int>(kChainReserve));
   if (e != hipSuccess) return e;
   // at most one workgroup (a segment of four waves, one per SIMD) per compute unit
-  chain_workers<<<cus > 0 ? cus : 256, kThreads, kChainReserve, s>>>(in, L, P, group);
+  chain_workers<<<cus > 0 ? cus : 256, kThreads, kChainReserve, s>>>(in, L, P, group, store ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -402,7 +402,8 @@ hipError_t launch_prep(const Inputs& in, const Layout& L, const Pointers& P, hip
 hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s);
 // sorts the utterances and cuts them into `groups` groups (see GroupQ)
 hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P, int groups, hipStream_t s);
-hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s);
+// store: keep alpha, beta and the block offsets for the posteriors (false: the loss only)
+hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, int group, bool store, hipStream_t s);
 hipError_t launch_weights(const Inputs& in, const Layout& L, const Pointers& P, float* losses_out, float* reduced_out,
                           hipStream_t s);
 hipError_t launch_classes(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);

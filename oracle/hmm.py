@@ -9,6 +9,10 @@ are the extended label sequence (blank, l1, blank, ..., lU, blank), whose transi
 advance by one, and skip by two into a label that differs from the label two states back, whose
 initial mass sits on the first two states and whose accepting states are the last two.
 Nothing here shares code with the banded recursion in ``ctc_oracle.c``.
+
+``hmm_model_loglik`` is the page's HMM module itself (normalised initial, transition and emission
+log weights, then the forward per observation sequence), the reference for the GPU HMM forward;
+it is pinned by enumeration of every state path and by closed forms (tests/test_hmm_oracle.py).
 """
 
 from __future__ import annotations
@@ -66,3 +70,51 @@ def ctc_nll_via_hmm(lp: np.ndarray, target, blank: int) -> float:
     ext, A, init, accept = ctc_topology(target, blank)
     emis = lp[:, ext]
     return -hmm_forward_loglik(emis, A, init, accept)
+
+
+def _normalise(x: np.ndarray, axis: int) -> np.ndarray:
+    return x - _lse(x, axis=axis)[..., None] if x.ndim > 1 else x - _lse(x)
+
+
+def hmm_model_loglik(log_init, log_trans, log_emit, observations) -> np.ndarray:
+    """The POPCORNBENCH page's HMM module, in float64: normalise the initial log weights over states,
+    each transition row over next states and each emission row over symbols (subtract the
+    log-sum-exp), then per sequence alpha_0 = log_pi + log_B[:, o_0],
+    alpha_t[j] = logsumexp_i(alpha_{t-1}[i] + log_A[i, j]) + log_B[j, o_t], and the log-likelihood is
+    the log-sum-exp of the last alpha over all states.  observations (B, T) ints; returns (B,)."""
+    li = np.asarray(log_init, dtype=np.float64)
+    lt = np.asarray(log_trans, dtype=np.float64)
+    le = np.asarray(log_emit, dtype=np.float64)
+    obs = np.asarray(observations, dtype=np.int64)
+    log_pi = li - _lse(li)
+    log_A = _normalise(lt, 1)
+    log_B = _normalise(le, 1)
+    out = np.empty(obs.shape[0])
+    for b in range(obs.shape[0]):
+        emis = log_B[:, obs[b]].T  # (T, S)
+        out[b] = hmm_forward_loglik(emis, log_A, log_pi, np.ones(log_A.shape[0], dtype=bool))
+    return out
+
+
+def hmm_model_loglik_brute(log_init, log_trans, log_emit, observations) -> np.ndarray:
+    """The same quantity by enumerating every state path (tiny S and T only): log of the sum over
+    paths of pi[s_0] B[s_0, o_0] prod_t A[s_{t-1}, s_t] B[s_t, o_t], normalised parameters."""
+    import itertools
+
+    li = np.asarray(log_init, dtype=np.float64)
+    lt = np.asarray(log_trans, dtype=np.float64)
+    le = np.asarray(log_emit, dtype=np.float64)
+    pi = np.exp(li) / np.exp(li).sum()
+    A = np.exp(lt) / np.exp(lt).sum(axis=1, keepdims=True)
+    Bm = np.exp(le) / np.exp(le).sum(axis=1, keepdims=True)
+    obs = np.asarray(observations, dtype=np.int64)
+    S, out = A.shape[0], []
+    for seq in obs:
+        tot = 0.0
+        for path in itertools.product(range(S), repeat=len(seq)):
+            p = pi[path[0]] * Bm[path[0], seq[0]]
+            for t in range(1, len(seq)):
+                p *= A[path[t - 1], path[t]] * Bm[path[t], seq[t]]
+            tot += p
+        out.append(np.log(tot))
+    return np.array(out)

@@ -227,6 +227,26 @@ def main():
         "roofline": roofline,
     }
 
+    # the second workload of the library: the dense HMM forward at the HMM page's size
+    # (S = 16 states, T = 128 frames, B = 64 sequences, O = 64 symbols), HIP events on the stream
+    hrng = np.random.default_rng(16)
+    hS, hT, hB, hO = 16, 128, 64, 64
+    h_in = [torch.from_numpy(hrng.normal(0, 1, size=sh).astype(np.float32)).to(dev) for sh in ((hS,), (hS, hS), (hS, hO))]
+    h_obs = torch.from_numpy(hrng.integers(0, hO, size=(hB, hT)).astype(np.int32)).to(dev)
+    for _ in range(5):
+        api.hmm_forward(*h_in, h_obs)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hreps = 200
+    ev0.record(stream)
+    for _ in range(hreps):
+        api.hmm_forward(*h_in, h_obs)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    h_us = ev0.elapsed_time(ev1) * 1e3 / hreps
+    out["hmm_forward"] = {"workload": f"S={hS} T={hT} B={hB} O={hO} float32", "us_per_call": h_us,
+                          "sequences_per_s": hB / (h_us * 1e-6), "frames_per_s": hB * hT / (h_us * 1e-6),
+                          "bound": "latency of T dependent log-semiring matrix-vector steps"}
+
     if not args.no_cpu_baseline:
         from oracle import oracle
 

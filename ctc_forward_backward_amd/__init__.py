@@ -5,7 +5,7 @@ loaded lazily so that the input generators in ``workloads`` import without the H
 """
 
 _API = ("packed_ctc_loss", "packed_ctc_forward", "packed_ctc_backward", "ctc_loss", "PackedCTCLoss", "packed_ctc_reduce",
-        "packed_ctc_workspace_size", "PackedCTCError", "library_path")
+        "packed_ctc_workspace_size", "PackedCTCError", "library_path", "hmm_forward")
 
 
 def __getattr__(name):

@@ -402,6 +402,12 @@ hipError_t launch_prep(const Inputs& in, const Layout& L, const Pointers& P, hip
 hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s);
 // sorts the utterances and cuts them into `groups` groups (see GroupQ)
 hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P, int groups, hipStream_t s);
+// dense log-space HMM forward (hmm.hip): one log-likelihood per observation sequence
+hipError_t launch_hmm_forward(const float* log_init, const float* log_trans, const float* log_emit, const void* obs,
+                              int obs_i64, int64_t B, int64_t T, int S, int O, float* out, hipStream_t s);
+constexpr int kHmmMaxStates = 64;
+constexpr int64_t kHmmMaxTable = 16384;  // S * O floats of the emission table in LDS
+
 // store: keep alpha, beta and the block offsets for the posteriors (false: the loss only)
 hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, int group, bool store, hipStream_t s);
 hipError_t launch_weights(const Inputs& in, const Layout& L, const Pointers& P, float* losses_out, float* reduced_out,

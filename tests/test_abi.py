@@ -15,16 +15,21 @@ HEADER = os.path.join(ROOT, "include", "packed_ctc.h")
 
 
 def _declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(packed_ctc_\w+)\s*\(", src)))
+    import glob
+
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\w[\w\s\*]*?\b((?:packed_ctc|hmm)_\w+)\s*\(", src, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("packed_ctc_loss", "packed_ctc_reduce", "packed_ctc_workspace_size", "packed_ctc_last_error",
               "packed_ctc_max_target_length", "packed_ctc_limits", "packed_ctc_version",
-              "packed_ctc_set_phase_timing", "packed_ctc_phase_times", "packed_ctc_workspace_status"):
+              "packed_ctc_set_phase_timing", "packed_ctc_phase_times", "packed_ctc_workspace_status",
+              "packed_ctc_forward", "packed_ctc_backward", "hmm_forward_loglik"):
         assert n in names
 
 
@@ -169,3 +174,24 @@ def test_autograd_binding_checks_without_gpu():
         api.ctc_loss(lp, *args, blank=0)
     with pytest.raises(ValueError, match="shape"):
         api.ctc_loss(torch.zeros(2, 5, 5, requires_grad=True), *args, blank=0)
+
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(B=-1), api.ERR_SHAPE, "batch"),
+    (dict(S=0), api.ERR_LIMIT, "states"),
+    (dict(S=65), api.ERR_LIMIT, "states"),
+    (dict(O=0), api.ERR_LIMIT, "S * O"),
+    (dict(S=64, O=300), api.ERR_LIMIT, "S * O"),
+    (dict(T=0), api.ERR_SHAPE, "frame"),
+    (dict(i64=2), api.ERR_ARG, "observations_i64"),
+    (dict(out=None), api.ERR_ARG, "NULL"),
+])
+def test_hmm_host_checks(kw, code, needle):
+    lib = api._load()
+    d = ctypes.c_void_p(0x1000)
+    a = dict(B=4, T=8, S=16, O=64, i64=0, out=d)
+    a.update(kw)
+    rc = lib.hmm_forward_loglik(d, d, d, d, a["i64"], a["B"], a["T"], a["S"], a["O"], a["out"], None)
+    assert rc == code
+    assert needle in lib.packed_ctc_last_error().decode()

@@ -293,7 +293,7 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
         const float l1 = log2_fast(1.0f + exp2_fast(-fabsf(d1)));
         const float h1 = __builtin_amdgcn_fmed3f(xb, n, 3.0e38f);
         const float t = h1 + l1;
-        const float nb = (h1 + lanef(ebv, i)) + l1;
+        const float nb = t + lanef(ebv, i);
         const float a2 = sk ? t : xb;
         const float d2 = xl - a2;
         const float l2 = log2_fast(1.0f + exp2_fast(-fabsf(d2)));

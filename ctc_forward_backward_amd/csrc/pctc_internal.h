@@ -207,6 +207,20 @@ __device__ __forceinline__ void wave_share(const Pointers& P, int g, int64_t wid
 // Chunk q holds flat elements [8q, 8q+8): 16 aligned bytes for 16-bit dtypes, 32 for float32, 64 for
 // float64 (read into float32 arithmetic; the gradient goes back as float64).
 
+// Row chunks are read once and written once: non-temporal loads and stores keep them from
+// displacing reused data (the recursions' states, class sums) in the caches.
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  const u32x4_nt v = __builtin_nontemporal_load(static_cast<const u32x4_nt*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void st_stream(void* p, uint4 v) {
+  const u32x4_nt w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, static_cast<u32x4_nt*>(p));
+}
+
 // Raw bytes of one chunk, held while its load is in flight.
 template <int DT>
 struct Raw8 {
@@ -216,17 +230,10 @@ struct Raw8 {
 template <int DT>
 __device__ __forceinline__ Raw8<DT> ld8(const void* base, int64_t q) {
   Raw8<DT> r;
-  if constexpr (DT == kF64) {
-    const uint4* p = static_cast<const uint4*>(base) + 4 * q;
+  constexpr int n = DT == kF64 ? 4 : (DT == kF32 ? 2 : 1);
+  const uint4* p = static_cast<const uint4*>(base) + n * q;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.u[i] = p[i];
-  } else if constexpr (DT == kF32) {
-    const uint4* p = static_cast<const uint4*>(base) + 2 * q;
-    r.u[0] = p[0];
-    r.u[1] = p[1];
-  } else {
-    r.u[0] = static_cast<const uint4*>(base)[q];
-  }
+  for (int i = 0; i < n; ++i) r.u[i] = ld_stream(p + i);
   return r;
 }
 
@@ -265,13 +272,15 @@ __device__ __forceinline__ void store8(void* base, int64_t q, const float v[8]) 
     for (int i = 0; i < 4; ++i) {
       const uint64_t a = __builtin_bit_cast(uint64_t, static_cast<double>(v[2 * i]));
       const uint64_t b = __builtin_bit_cast(uint64_t, static_cast<double>(v[2 * i + 1]));
-      p[i] = make_uint4(static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32), static_cast<uint32_t>(b),
-                        static_cast<uint32_t>(b >> 32));
+      st_stream(p + i, make_uint4(static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32), static_cast<uint32_t>(b),
+                                  static_cast<uint32_t>(b >> 32)));
     }
   } else if constexpr (DT == kF32) {
-    float4* p = static_cast<float4*>(base) + 2 * q;
-    p[0] = make_float4(v[0], v[1], v[2], v[3]);
-    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+    uint4* p = static_cast<uint4*>(base) + 2 * q;
+    st_stream(p, make_uint4(__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1]),
+                            __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3])));
+    st_stream(p + 1, make_uint4(__builtin_bit_cast(uint32_t, v[4]), __builtin_bit_cast(uint32_t, v[5]),
+                                __builtin_bit_cast(uint32_t, v[6]), __builtin_bit_cast(uint32_t, v[7])));
   } else {
     uint32_t w[4];
 #pragma unroll
@@ -286,7 +295,7 @@ __device__ __forceinline__ void store8(void* base, int64_t q, const float v[8]) 
       }
       w[i] = lo | (hi << 16);
     }
-    static_cast<uint4*>(base)[q] = make_uint4(w[0], w[1], w[2], w[3]);
+    st_stream(static_cast<uint4*>(base) + q, make_uint4(w[0], w[1], w[2], w[3]));
   }
 }
 

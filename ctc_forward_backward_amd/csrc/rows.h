@@ -20,8 +20,8 @@
 //     exp(alpha + beta - lp + nll) for a feasible utterance, with the rounding drift of the
 //     recursions divided out).  The row's class sums, times w / z, are written compactly: U+1
 //     floats per row.
-//   - dense_row: the whole row (up to 16 aligned 16-byte chunks per lane) and its compact class
-//     sums are loaded together; the row is streamed once, and a per-utterance class bitmap with
+//   - dense_row: the row in batches of aligned 16-byte chunks (the first batch loaded together with
+//     the row's compact class sums); the row is streamed once, and a per-utterance class bitmap with
 //     per-word prefix counts (in LDS) tells which columns of a chunk carry a class and its rank,
 //     so the correction is applied in registers before the single store.
 #pragma once
@@ -35,9 +35,11 @@ constexpr int kBlocks = 4;  // state-pair blocks whose loads are issued together
 constexpr int kLook = 4;    // row chunks whose class lookups are issued together
 constexpr int kPost = 8;    // compact class sums per lane held in registers (U+1 <= 512)
 
-// aligned 8-element row chunks per lane loaded at once (the whole row for D <= 8192 at 2 bytes)
+// aligned 8-element row chunks per lane loaded at once.  Four, not a whole row: fewer registers
+// let more waves stream rows side by side, which measured faster than more bytes in flight per
+// wave (a large-vocabulary group: 139 us at 4 chunks, 136 at 8, 153 at 16)
 template <int DT>
-constexpr int row_batch() { return DT == kF64 ? 4 : (DT == kF32 ? 8 : 16); }
+constexpr int row_batch() { return 4; }
 
 // a row gets a gradient from its utterance only if the utterance has a non-zero weight and an
 // alignment (a NaN input makes the loss NaN, which also fails the test)

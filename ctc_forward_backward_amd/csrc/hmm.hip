@@ -6,7 +6,8 @@
 // It is the dense-topology form of the recursion the CTC path runs banded.
 //
 // Design for gfx950 (not the page's one-thread-per-state CUDA block):
-//   - One wave per sequence, lane j holding state j (S <= 64).  A step is a matrix-vector product
+//   - One wave per sequence.  For S <= 16, four lanes per state (below); otherwise lane j holds
+//     state j (S <= 64).  A step is a matrix-vector product
 //     in the log semiring: lane j needs every alpha_{t-1}[i].  v_readlane broadcasts alpha_{t-1}[i]
 //     as a scalar operand, so lane j forms alpha[i] + log A[i][j] against its own column of A held
 //     in registers, takes the maximum and sums 2^(x - max): no LDS traffic and no barrier in the
@@ -127,6 +128,95 @@ __global__ void __launch_bounds__(256) hmm_forward_kernel(const float* __restric
   if (lane == 0) out[b] = ll < -1e29f ? -INFINITY : ll * kLn2;
 }
 
+// S <= 16: four lanes per state.  Lane 4j + q holds state j and takes the terms i = q, q+4, q+8,
+// q+12 of its log-sum-exp (alpha_{t-1}[i] fetched by ds_bpermute from lane 4i); the maximum and
+// then the sum of a state's terms are reduced over its quad with quad-permute DPP moves, so every
+// lane of the quad ends with the state's new alpha.  A step is then a quarter of the
+// one-lane-per-state work.
+template <int CTRL>
+__device__ __forceinline__ float quad_swap(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                                               CTRL, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float from_lane(float x, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src * 4, __builtin_bit_cast(int, x)));
+}
+
+__global__ void __launch_bounds__(256) hmm_forward16_kernel(const float* __restrict__ log_init,
+                                                            const float* __restrict__ log_trans,
+                                                            const float* __restrict__ log_emit, const void* obs,
+                                                            int obs_i64, int64_t B, int64_t T, int S, int O,
+                                                            float* __restrict__ out) {
+  extern __shared__ float le2[];  // (S, O) normalised base-2 emission log weights
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int s = w; s < S; s += 4) {
+    const float* row = log_emit + (int64_t)s * O;
+    float m = kFloorH;
+    for (int o = lane; o < O; o += 64) m = fmaxf(m, row[o] * kLog2e);
+    m = wave_max64(m);
+    float sum = 0.0f;
+    for (int o = lane; o < O; o += 64) sum += exp2_fast(row[o] * kLog2e - m);
+    const float lse = m + log2_fast(wave_sum64(sum));
+    for (int o = lane; o < O; o += 64) le2[s * O + o] = fmaxf(row[o] * kLog2e - lse, kFloorH);
+  }
+  const int j = lane >> 2, q = lane & 3;
+  const bool on = j < S;
+  const bool lead = on && q == 0;  // the lane that stands for state j in sums over states
+  float pi = kFloorH;
+  if (on) pi = fmaxf(log_init[j] * kLog2e, kFloorH);
+  const float pil = wave_lse2(lead ? pi : kFloorH);
+  pi = on ? fmaxf(pi - pil, kFloorH) : kFloorH;
+  float rowlse = 0.0f;  // lane 4i: the log-sum-exp of transition row i
+  if (lead) {
+    const float* row = log_trans + (int64_t)j * S;
+    float m = kFloorH;
+    for (int k = 0; k < S; ++k) m = fmaxf(m, row[k] * kLog2e);
+    float sum = 0.0f;
+    for (int k = 0; k < S; ++k) sum += exp2_fast(row[k] * kLog2e - m);
+    rowlse = m + log2_fast(sum);
+  }
+  float a2[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = q + 4 * k;
+    const float ri = from_lane(rowlse, 4 * i);
+    a2[k] = kFloorH;
+    if (on && i < S) a2[k] = fmaxf(log_trans[(int64_t)i * S + j] * kLog2e - ri, kFloorH);
+  }
+  __syncthreads();  // the emission table is complete
+
+  const int64_t b = (int64_t)blockIdx.x * 4 + w;
+  if (b >= B) return;
+  const int64_t base = b * T;
+  int sym = symbol(obs, obs_i64, base + min((int64_t)lane, T - 1), O);  // frames [0, 64)
+  int nxt = sym;
+  const int erow = on ? j * O : 0;  // every lane reads inside the table
+  float alpha = fmaxf(pi + le2[erow + __builtin_amdgcn_readlane(sym, 0)], kFloorH);
+  if (!on) alpha = kFloorH;
+  for (int64_t t = 1; t < T; ++t) {
+    const int k64 = static_cast<int>(t & 63);
+    if (k64 == 0) sym = nxt;
+    if (k64 == 1) nxt = symbol(obs, obs_i64, base + min(t - 1 + 64 + lane, T - 1), O);
+    const float e = le2[erow + __builtin_amdgcn_readlane(sym, k64)];
+    float x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = from_lane(alpha, 4 * (q + 4 * k)) + a2[k];
+    // the state's maximum over its 16 terms first (quad_perm [1,0,3,2] then [2,3,0,1]), so the
+    // partial sums share it and merge by plain addition
+    float m = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    m = fmaxf(m, quad_swap<0xB1>(m));
+    m = fmaxf(m, quad_swap<0x4E>(m));
+    float sum = (exp2_fast(x[0] - m) + exp2_fast(x[1] - m)) + (exp2_fast(x[2] - m) + exp2_fast(x[3] - m));
+    sum += quad_swap<0xB1>(sum);
+    sum += quad_swap<0x4E>(sum);
+    alpha = on ? fmaxf(m + log2_fast(sum) + e, kFloorH) : kFloorH;
+  }
+  const float ll = wave_lse2(lead ? alpha : kFloorH);
+  if (lane == 0) out[b] = ll < -1e29f ? -INFINITY : ll * kLn2;
+}
+
 }  // namespace
 
 hipError_t launch_hmm_forward(const float* log_init, const float* log_trans, const float* log_emit, const void* obs,
@@ -143,7 +233,7 @@ hipError_t launch_hmm_forward(const float* log_init, const float* log_trans, con
     kernel<<<grid, 256, lds, s>>>(log_init, log_trans, log_emit, obs, obs_i64, B, T, S, O, out);
     return hipGetLastError();
   };
-  if (S <= 16) return launch(&hmm_forward_kernel<16>);
+  if (S <= 16) return launch(&hmm_forward16_kernel);
   if (S <= 32) return launch(&hmm_forward_kernel<32>);
   return launch(&hmm_forward_kernel<64>);
 }

@@ -132,14 +132,6 @@ __device__ __forceinline__ float lse2(float a, float b) {
   return hi + log2_fast(1.0f + exp2_fast(lo - hi));
 }
 
-// log2(2^a + 2^b + 2^c)
-__device__ __forceinline__ float lse3(float a, float b, float c) {
-  const float hi = fmaxf(fmaxf(a, b), c);
-  const float lo = fminf(fminf(a, b), c);
-  const float mid = __builtin_amdgcn_fmed3f(a, b, c);
-  return hi + log2_fast(1.0f + exp2_fast(mid - hi) + exp2_fast(lo - hi));
-}
-
 __device__ __forceinline__ float load_lp(const void* p, int dtype, int64_t i) {
   if (dtype == kF32) return static_cast<const float*>(p)[i];
   if (dtype == kF64) return static_cast<float>(static_cast<const double*>(p)[i]);
@@ -426,8 +418,6 @@ hipError_t launch_posteriors(const Inputs& in, const Layout& L, const Pointers& 
 hipError_t launch_dense(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, int group, hipStream_t s);
 // zero gradient rows owned by no utterance
 hipError_t launch_gaps(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s);
-hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
-hipError_t launch_zero_bytes(void* p, int64_t nbytes, hipStream_t s);
 hipError_t launch_reduce(const float* losses, const void* target_lengths, bool i64, int64_t B, int reduction, float* out,
                          hipStream_t s);
 

@@ -16,16 +16,8 @@ __global__ void fill_i32_kernel(int* p, int64_t n, int v) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
-__global__ void fill_f32_kernel(float* p, int64_t n, float v) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
-}
-
 __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0u;
-}
-
-__global__ void zero_u8_kernel(uint8_t* p, int64_t n) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
 }
 
 // One workgroup per utterance: clamp the metadata so that every later access stays in bounds,
@@ -416,21 +408,6 @@ hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P,
 hipError_t launch_weights(const Inputs& in, const Layout& L, const Pointers& P, float* losses_out, float* reduced_out,
                           hipStream_t s) {
   weights_kernel<<<1, 256, 0, s>>>(in, L, P, losses_out, reduced_out);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
-  if (n > 0) fill_f32_kernel<<<grid_for(n, 256), 256, 0, s>>>(p, n, v);
-  return hipGetLastError();
-}
-
-hipError_t launch_zero_bytes(void* p, int64_t nbytes, hipStream_t s) {
-  if (nbytes <= 0) return hipGetLastError();
-  if ((reinterpret_cast<uintptr_t>(p) & 3) == 0 && (nbytes & 3) == 0) {
-    zero_u32_kernel<<<grid_for(nbytes / 4, 256), 256, 0, s>>>(static_cast<uint32_t*>(p), nbytes / 4);
-  } else {
-    zero_u8_kernel<<<grid_for(nbytes, 256), 256, 0, s>>>(static_cast<uint8_t*>(p), nbytes);
-  }
   return hipGetLastError();
 }
 

@@ -221,6 +221,37 @@ def main():
         "roofline": roofline,
     }
 
+    # per-call medians with HIP events around single calls: warm (back to back) and cold (L2 and
+    # MALL flushed by writing a 512 MB buffer before each call); and the attainable rate, a 1 GB
+    # device-to-device copy
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2 * 10)]
+    for k, (e0, e1) in enumerate(evs):
+        if k >= 10:
+            flush.fill_(k & 0xff)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    warm = sorted(e0.elapsed_time(e1) for e0, e1 in evs[:10])
+    cold = sorted(e0.elapsed_time(e1) for e0, e1 in evs[10:])
+    del flush
+    csrc_ = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cdst_ = torch.empty_like(csrc_)
+    cdst_.copy_(csrc_)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        cdst_.copy_(csrc_)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del csrc_, cdst_
+    out["call_medians_ms"] = {"warm": warm[len(warm) // 2], "cold_l2_mall_flushed": cold[len(cold) // 2],
+                              "calls": 10}
+    out["call_hbm"]["device_copy_gbps"] = copy_gbps
+    out["call_hbm"]["frac_of_device_copy"] = call_gbps / copy_gbps
+
     # the second workload of the library: the dense HMM forward at the HMM page's size
     # (S = 16 states, T = 128 frames, B = 64 sequences, O = 64 symbols), HIP events on the stream
     hrng = np.random.default_rng(16)

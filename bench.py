@@ -289,9 +289,19 @@ def main():
             ref = oracle.ctc_batch(b)
             t_cpu += time.perf_counter() - c0
             runs += 1
+        c0 = time.perf_counter()
+        oracle.ctc_batch(b, nthreads=1)
+        t_one = time.perf_counter() - c0
+        cpu_model = ""
+        try:
+            with open("/proc/cpuinfo") as fh:
+                cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+        except OSError:
+            pass
         out["cpu_baseline"] = {
             "value": T_total * runs / t_cpu, "unit": "frames/s", "cores": oracle.max_threads(), "kind": "oracle",
             "sample": f"the whole {b.name} batch ({T_total} frames, D={D}), loss + gradient in float64, {runs} run(s)",
+            "one_thread_value": T_total / t_one, "cpu_model": cpu_model,
         }
         fin = np.isfinite(ref["loss"])
         rel = np.abs(gpu_losses[fin] - ref["loss"][fin]) / np.maximum(np.abs(ref["loss"][fin]), 1e-30)

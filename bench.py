@@ -225,16 +225,17 @@ def main():
     # MALL flushed by writing a 512 MB buffer before each call); and the attainable rate, a 1 GB
     # device-to-device copy
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2 * 10)]
+    nmed = 20
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2 * nmed)]
     for k, (e0, e1) in enumerate(evs):
-        if k >= 10:
+        if k >= nmed:
             flush.fill_(k & 0xff)
         e0.record(stream)
         step()
         e1.record(stream)
     torch.cuda.synchronize()
-    warm = sorted(e0.elapsed_time(e1) for e0, e1 in evs[:10])
-    cold = sorted(e0.elapsed_time(e1) for e0, e1 in evs[10:])
+    warm = sorted(e0.elapsed_time(e1) for e0, e1 in evs[:nmed])
+    cold = sorted(e0.elapsed_time(e1) for e0, e1 in evs[nmed:])
     del flush
     csrc_ = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cdst_ = torch.empty_like(csrc_)
@@ -248,7 +249,7 @@ def main():
     copy_gbps = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del csrc_, cdst_
     out["call_medians_ms"] = {"warm": warm[len(warm) // 2], "cold_l2_mall_flushed": cold[len(cold) // 2],
-                              "calls": 10}
+                              "calls": nmed}
     out["call_hbm"]["device_copy_gbps"] = copy_gbps
     out["call_hbm"]["frac_of_device_copy"] = call_gbps / copy_gbps
 
@@ -302,6 +303,7 @@ def main():
             "value": T_total * runs / t_cpu, "unit": "frames/s", "cores": oracle.max_threads(), "kind": "oracle",
             "sample": f"the whole {b.name} batch ({T_total} frames, D={D}), loss + gradient in float64, {runs} run(s)",
             "one_thread_value": T_total / t_one, "cpu_model": cpu_model,
+            "gbps_over_counted_bytes": bytes_call * runs / t_cpu / 1e9,
         }
         fin = np.isfinite(ref["loss"])
         rel = np.abs(gpu_losses[fin] - ref["loss"][fin]) / np.maximum(np.abs(ref["loss"][fin]), 1e-30)

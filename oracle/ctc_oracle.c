@@ -193,8 +193,9 @@ int ctc_oracle(const double* lp, int64_t T_total, int64_t D, const int64_t* cu, 
     }
     int failed = 0;
 #ifdef _OPENMP
-    if (nthreads > 0) omp_set_num_threads(nthreads);
-#pragma omp parallel for schedule(dynamic, 1)
+    /* a thread count for this call only (0: the runtime's default); it does not change later calls */
+    const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
 #endif
     for (int64_t i = 0; i < B; ++i) {
         const int64_t b = order[i];

@@ -112,6 +112,10 @@ int packed_ctc_max_target_length(const void* target_lengths, int index_flags, in
  * max_target_length < 0: the library reads target_lengths on the host exactly as
  *   packed_ctc_max_target_length does, except while `stream` is being captured, where
  *   target_width stands in ([PR] `packed_ctc_loss`: no host read under graph capture).
+ * Streams: large batches run in up to three length-sorted groups, two of them on streams of the
+ *   library's own (created on the first such call on a device, forked from and joined back into
+ *   `stream` with events, so the call stays ordered on `stream` and is graph-capturable).  A call
+ *   captured before that device's streams exist runs as one group on `stream`.
  * The workspace must be at least packed_ctc_workspace_size(T_total, D, B, bound) bytes, bound =
  *   max_target_length if >= 0 else target_width, and 256-byte aligned.
  * log_probs and grad_out must be 16-byte aligned (PCTC_ERR_ARG otherwise).

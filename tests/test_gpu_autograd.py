@@ -212,3 +212,46 @@ def test_graph_capture_autograd(api):
         assert torch.allclose(out.detach(), ref_out.detach(), rtol=1e-6, atol=0), k
         assert float((lp_static.grad.double() - ref_lp.grad.double()).abs().max()) <= 1e-6, k
         _say(f"  replay {k}: matches the eager forward + backward")
+
+
+_FIRST_CALL_CAPTURED = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import numpy as np, torch
+from ctc_forward_backward_amd import api, workloads as W
+b = W.make_workload("small")  # three utterance groups
+dev = torch.device("cuda:0")
+args = (b.cu_seqlens.to(dev), b.lengths.to(dev), b.targets.to(dev), b.target_lengths.to(dev))
+kw = dict(blank=b.blank, zero_infinity=b.zero_infinity, reduction=b.reduction, max_target_length=int(b.targets.shape[1]))
+lp = b.log_probs.to(dev).clone()
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g):  # the process's first library call: no library streams exist yet
+    losses, reduced, grad = api.packed_ctc_loss(lp, *args, **kw)
+for k in range(2):
+    rng = np.random.default_rng(200 + k)
+    logits = rng.normal(0.0, 2.0, size=tuple(lp.shape))
+    fresh = torch.from_numpy(logits).log_softmax(-1).to(lp.dtype).to(dev)
+    lp.copy_(fresh)
+    g.replay()
+    torch.cuda.synchronize()
+    el, er, eg = api.packed_ctc_loss(fresh, *args, **kw)
+    torch.cuda.synchronize()
+    assert torch.allclose(losses, el, rtol=1e-6, atol=0), k
+    assert float((grad.double() - eg.double()).abs().max()) <= 1e-6, k
+print("OK", flush=True)
+"""
+
+
+def test_graph_capture_as_first_call(api):
+    """A call captured before the library has made its group streams runs as one group on the
+    capturing stream; replays match eager calls.  Runs in a child process, so that no earlier call
+    has made the streams."""
+    import os
+    import subprocess
+    import sys
+
+    _say("[gpu autograd] graph capture as a process's first call (child process)")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _FIRST_CALL_CAPTURED, root], capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0 and "OK" in r.stdout, (r.stdout[-2000:], r.stderr[-2000:])

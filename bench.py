@@ -196,6 +196,16 @@ def main():
                     "work_per_call": f"{T_total} rows x {D} x ({bpe} B read + {bpe} B written)"}
     else:
         roofline = None
+    # the HBM-bound kernel beside it: the gradient rows, counted bytes over their summed launch
+    # time per call (a time-weighted average over the group launches, which share the device with
+    # the other groups' kernels)
+    roofline_rows = None
+    if "dense" in by_kernel and by_kernel["dense"] > 0:
+        t_rows = by_kernel["dense"] * 1e-3
+        a_rows = bytes_call / t_rows / 1e9
+        roofline_rows = {"bound": "hbm", "kernel": "dense", "achieved": a_rows, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": a_rows / HBM_PEAK_GBPS, "traffic": profiled_traffic(b.name, "dense"),
+                         "work_per_call": f"{T_total} rows x {D} x ({bpe} B read + {bpe} B written)"}
 
     out = {
         "metric": METRIC,
@@ -219,6 +229,7 @@ def main():
         "ms_per_step_with_phase_events": (tp1 - tp0) * 1e3 / args.steps,
         "kernel_ms_per_call": by_kernel,
         "roofline": roofline,
+        "roofline_rows": roofline_rows,
     }
 
     # per-call medians with HIP events around single calls: warm (back to back) and cold (L2 and

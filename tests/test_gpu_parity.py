@@ -261,3 +261,18 @@ def test_float64_inputs(api, oracle_mod, reduction):
     got = run_gpu(api, b)
     assert got["grad_dtype"] == torch.float64
     compare(got, oracle_mod.ctc_batch(b), torch.float64, f"f64/{reduction}")
+
+
+def test_maximum_sizes(api, oracle_mod):
+    """The library's limits: a target of 8191 labels (16383 states: 128 state blocks, 32 segments per
+    recursion) over 8800 frames, and D = 32768 classes with the blank at the last class."""
+    lim_u, lim_d = api.limits()
+    _say(f"[gpu parity] maximum sizes: U = {lim_u}, D = {lim_d}")
+    rng = np.random.default_rng(12)
+    targets = [[int(x) for x in rng.integers(1, 64, size=lim_u)], [int(x) for x in rng.integers(1, 64, size=7)]]
+    b = W.make_batch([8800, 30], targets, 64, seed=12, sigma=1.5, reduction="none")
+    compare(run_gpu(api, b), oracle_mod.ctc_batch(b), torch.float32, f"U={lim_u}")
+    targets = [[int(x) for x in rng.integers(0, lim_d - 1, size=u)] for u in (30, 12, 0)]
+    b = W.make_batch([90, 41, 5], targets, lim_d, seed=13, sigma=3.0, dtype="bf16", blank=lim_d - 1,
+                     reduction="mean")
+    compare(run_gpu(api, b), oracle_mod.ctc_batch(b), torch.bfloat16, f"D={lim_d}")

@@ -42,9 +42,10 @@
 //     one load of next chunk's label emission, both through buffer resources rebased per chunk so
 //     that every offset is a scalar register; the blank emissions of a chunk are one contiguous load,
 //     one frame per lane.
+#include <algorithm>
 #include <type_traits>
 
-#include "pctc_internal.h"
+#include "rows.h"
 
 namespace pctc {
 
@@ -56,6 +57,7 @@ constexpr int kWaves = kSegWaves;      // blocks per segment = waves per workgro
 constexpr int kThreads = 64 * kWaves;
 constexpr int kSpinLimit = 1 << 20;    // polls before a wave gives up waiting (about a second)
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
+constexpr int kStoreSc1 = 16;                 // cache policy of a buffer store: sc1, written through to device scope
 static_assert(2 * kK + 1 <= kEPad, "emission padding must cover two chunks of prefetch");
 static_assert(kR % kK == 0, "a chunk's ring slots must not wrap");
 
@@ -186,6 +188,7 @@ struct Ctx {
   int* sig;                 // this block's offset per chunk, at the row of the chunk's first frame
   float* ab;                // this block's 128 states per row (row 0)
   bool store;               // keep the states and offsets (false: loss only, nothing is written)
+  int* prog;                // streamed pipeline, the chain's last block: where it publishes its stored steps
   int* err;
   const Inputs* in;
   int64_t B;
@@ -193,7 +196,16 @@ struct Ctx {
 
 // The recursion of one block, specialised on the direction and on the kinds of its links, so that
 // the frame loop carries no branch on any of them.
-template <bool BETA, bool IN_GLOBAL, bool OUT_GLOBAL>
+//
+// STREAM (the streamed pipeline, where the posteriors of a frame are formed on other compute units,
+// possibly other XCDs, while the recursions still run): the states are stored write-through to the
+// device-coherent level (sc1) and the offsets with device-scope stores, and the chain's last block
+// (every other block of the chain is at least one chunk ahead of it) publishes how many steps are
+// stored.  At the start of chunk c it publishes the steps through chunk c-3: a wave has at most 63
+// vector-memory operations in flight and issues at least 64 per chunk (a label-emission load and a
+// state store per frame), so by then every store of chunk c-2 and before has completed.  The last
+// publication is a device-scope release after the last frame.
+template <bool BETA, bool IN_GLOBAL, bool OUT_GLOBAL, bool STREAM>
 __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
   const int lane = cx.lane, k = cx.k, T = cx.T, U = cx.U;
   const int edge = BETA ? 0 : 63;
@@ -220,9 +232,16 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
     xl = (first && cx.vl) ? el : kNeg;
     // beta is stored without the frame's own emission (the empty sum 0 at its start states), so that
     // alpha + stored beta is the posterior's exponent with no emission to take out
-    if (cx.store)
-      *reinterpret_cast<float2*>(cx.ab + r * 128 + 2 * lane) =
-          BETA ? make_float2((first && cx.vl) ? 0.0f : kNeg, first ? 0.0f : kNeg) : make_float2(xb, xl);
+    if (cx.store) {
+      const float2 v0 = BETA ? make_float2((first && cx.vl) ? 0.0f : kNeg, first ? 0.0f : kNeg) : make_float2(xb, xl);
+      if (STREAM) {
+        const __amdgpu_buffer_rsrc_t ab0 = __builtin_amdgcn_make_buffer_rsrc(cx.ab + r * 128, 0, 512, kRsrcWord3);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{__builtin_bit_cast(uint32_t, v0.x), __builtin_bit_cast(uint32_t, v0.y)},
+                                              ab0, lane * 8, 0, kStoreSc1);
+      } else {
+        *reinterpret_cast<float2*>(cx.ab + r * 128 + 2 * lane) = v0;
+      }
+    }
     if (lane == edge) {
       const unsigned long long v = pack(xl, slot_hi(0.0f, -1));
       if (OUT_GLOBAL) gstore(cx.gout + r, v);
@@ -263,7 +282,15 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
       const bool check_cons = !OUT_GLOBAL && cx.lout_live && c >= kR / kK - 1;
       const int cons = check_cons ? __hip_atomic_load(cx.prog_cons, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0;
       const float ebn = P.Eb[row(1 + (int64_t)(c + 1) * kK + lk)];
-      if (cx.store) cx.sig[row(1 + (int64_t)c * kK)] = static_cast<int>(off);
+      if (cx.store) {
+        if (STREAM)
+          __hip_atomic_store(cx.sig + row(1 + (int64_t)c * kK), static_cast<int>(off), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        else
+          cx.sig[row(1 + (int64_t)c * kK)] = static_cast<int>(off);
+      }
+      if (STREAM && cx.prog && c >= 3 && lane == 0)
+        __hip_atomic_store(cx.prog, (c - 2) * kK + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (IN_GLOBAL) {
         if (__ballot(need && !global_ok(raw))) raw = wait_global(cx.gin + row(min(c * kK + lk, nsteps)), raw, need, err);
         hraw = cx.no_in ? none : gload(cx.gin + row(min((c + 1) * kK + lk, nsteps)));
@@ -307,7 +334,7 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
         xl = nl;
         const u32x2 st = BETA ? u32x2{__builtin_bit_cast(uint32_t, pl), __builtin_bit_cast(uint32_t, t)}
                               : u32x2{__builtin_bit_cast(uint32_t, xb), __builtin_bit_cast(uint32_t, xl)};
-        __builtin_amdgcn_raw_buffer_store_b64(st, ab, lane * 8, in_chunk(i) * 512, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(st, ab, lane * 8, in_chunk(i) * 512, STREAM ? kStoreSc1 : 0);
         if (lane == edge) {
           const unsigned long long v = pack(xl, hi);
           if (OUT_GLOBAL) gstore(gslot + drow * i, v);
@@ -330,6 +357,7 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
     for (int c = 1; c < nfull; ++c) run_chunk(std::true_type{}, c, kK);
     if (nrem > 0) run_chunk(std::false_type{}, nfull, nrem);
   }
+  if (STREAM && cx.prog && lane == 0) __hip_atomic_store(cx.prog, T, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 
   // ---- likelihood: the block holding the last states (alpha) or the first states (beta) ----
   const bool owner = BETA ? (cx.j == 0) : (cx.j == (U >> 6));
@@ -368,6 +396,7 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
 }
 
 // One block (this wave) of segment `seg` of chain (utterance, direction).
+template <bool STREAM>
 __device__ __forceinline__ void run_wave(const Inputs& in, const Layout& L, const Pointers& P, Shared& sh, int chain,
                                          int seg, int w, int lane, bool store) {
   Ctx cx;
@@ -410,6 +439,7 @@ __device__ __forceinline__ void run_wave(const Inputs& in, const Layout& L, cons
   cx.sig = P.sig + (dir * Gm + j) * TT;
   cx.ab = P.AB + (dir * Gm + j) * TT * 128;
   cx.store = store;
+  cx.prog = (STREAM && (beta ? j == 0 : j == G - 1)) ? P.prog + chain : nullptr;
   cx.err = &P.ctl->err;
   cx.in = &in;
   cx.B = L.B;
@@ -417,19 +447,19 @@ __device__ __forceinline__ void run_wave(const Inputs& in, const Layout& L, cons
   __builtin_amdgcn_s_setprio(3);
   if (!beta) {
     if (in_global) {
-      if (out_global) run_block<false, true, true>(cx, P);
-      else run_block<false, true, false>(cx, P);
+      if (out_global) run_block<false, true, true, STREAM>(cx, P);
+      else run_block<false, true, false, STREAM>(cx, P);
     } else {
-      if (out_global) run_block<false, false, true>(cx, P);
-      else run_block<false, false, false>(cx, P);
+      if (out_global) run_block<false, false, true, STREAM>(cx, P);
+      else run_block<false, false, false, STREAM>(cx, P);
     }
   } else {
     if (in_global) {
-      if (out_global) run_block<true, true, true>(cx, P);
-      else run_block<true, true, false>(cx, P);
+      if (out_global) run_block<true, true, true, STREAM>(cx, P);
+      else run_block<true, true, false, STREAM>(cx, P);
     } else {
-      if (out_global) run_block<true, false, true>(cx, P);
-      else run_block<true, false, false>(cx, P);
+      if (out_global) run_block<true, false, true, STREAM>(cx, P);
+      else run_block<true, false, false, STREAM>(cx, P);
     }
   }
   __builtin_amdgcn_s_setprio(0);
@@ -452,9 +482,102 @@ __global__ void __launch_bounds__(kThreads, 1) chain_workers(Inputs in, Layout L
     const int idx = __builtin_amdgcn_readfirstlane(sh.item);
     if (idx >= qlen) break;
     const int item = __builtin_amdgcn_readfirstlane(items[idx]);
-    run_wave(in, L, P, sh, item >> 12, item & 4095, w, lane, store != 0);
+    run_wave<false>(in, L, P, sh, item >> 12, item & 4095, w, lane, store != 0);
     __syncthreads();
   }
+}
+
+// ---- streamed pipeline ----------------------------------------------------------------------------
+
+// bounded wait until a chain has published at least `steps` stored steps
+__device__ __forceinline__ void wait_steps(const int* prog, int steps, int* err) {
+  int spins = 0;
+  while (__hip_atomic_load(prog, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < steps) {
+    if (++spins > kSpinLimit || gave_up(err)) {
+      give_up(err);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(32);
+  }
+}
+
+// Band k of utterance b (see kBand): one wave waits until both recursions have passed the band (the
+// others wait at the barrier, so polling stays one load per workgroup and microsecond), then its
+// rows are shared out over the workgroup's waves, one row per wave at a time.  Each row: the posteriors into the wave's LDS, then the gradient row; a row of an
+// utterance with a NaN input, no alignment or a zero weight is filled (NaN, or 0 where the weight
+// is 0 -- under zero_infinity an utterance without alignment has weight 0).
+template <int DT>
+__device__ __forceinline__ void row_band(const Inputs& in, const Layout& L, const Pointers& P, void* grad,
+                                         uint32_t* lds, int b, int k, int w, int lane, int& cur_b) {
+  const Meta m = P.meta[b];
+  const int T = m.T;
+  const int ra = T / 2 + k * kBand, re = min(ra + kBand, T) - 1;  // its later steps max(t, T-1-t)
+  const int n1 = re - ra + 1;                                       // frames ra .. re
+  const int lo2 = T - 1 - re, hi2 = min(T - 1 - ra, ra - 1);        // and their mirrors
+  const int n = n1 + max(hi2 - lo2 + 1, 0);
+  if (w == 0) {
+    wait_steps(P.prog + 2 * b, re + 1, &P.ctl->err);
+    wait_steps(P.prog + 2 * b + 1, re + 1, &P.ctl->err);
+  }
+  __syncthreads();  // (also keeps the compiler from moving the row's loads above the wait)
+  if (w >= n) return;
+  const bool nan = m.flags & 1;
+  const float w0 = utterance_weight(in, L.B, b, false);
+  float* acc = reinterpret_cast<float*>(lds);
+  for (int i = w; i < n; i += kStreamWaves) {
+    const int t = i < n1 ? ra + i : lo2 + (i - n1);
+    const int64_t r = (int64_t)m.start + t;
+    if (!nan && w0 != 0.0f && rows::posterior_stream(L, P, acc, r, b, w0, lane)) {
+      rows::dense_row<DT, true>(in, L, P, grad, lds, r, b, w0, lane, cur_b);
+    } else {
+      const bool zero = w0 == 0.0f || (!nan && in.zero_infinity);
+      rows::fill_row<DT>(L, grad, r, zero ? 0.0f : __builtin_nanf(""), lane);
+    }
+  }
+}
+
+// One persistent workgroup per compute unit.  The queue holds the recursion segments (producers
+// first, longest utterances first), then the row bands, readiest first.  A segment runs on waves
+// 0-3 while the other twelve wait at the barrier; a band runs on all sixteen.  A band is claimed
+// only after every segment has been claimed by a running workgroup, so the recursions it waits for
+// always progress.
+template <int DT>
+__global__ void __launch_bounds__(64 * kStreamWaves, 1) stream_workers(Inputs in, Layout L, Pointers P, void* grad,
+                                                                       int per_wave) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char ssm[];
+  Shared& sh = *reinterpret_cast<Shared*>(ssm);
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint32_t* lds = reinterpret_cast<uint32_t*>(ssm + ((sizeof(Shared) + 15) & ~size_t(15))) + (int64_t)w * per_wave;
+  GroupQ* q = &P.ctl->g[0];
+  const int qlen = q->qlen, nbands = P.ctl->nbands;
+  const int* items = P.items + q->itemoff;
+  int cur_b = -1;
+  for (;;) {
+    for (int i = tid; i < kWaves * kR; i += 64 * kStreamWaves) (&sh.ring[0][0])[i] = 0ull;
+    if (tid < kWaves) sh.prog[tid] = -1;
+    if (tid == 0) sh.item = atomicAdd(&q->qcount, 1);
+    __syncthreads();
+    const int idx = __builtin_amdgcn_readfirstlane(sh.item);
+    if (idx >= qlen + nbands) break;
+    if (idx < qlen) {
+      if (w < kWaves) {
+        const int item = __builtin_amdgcn_readfirstlane(items[idx]);
+        run_wave<true>(in, L, P, sh, item >> 12, item & 4095, w, lane, true);
+      }
+    } else {
+      const int2 bd = P.bands[idx - qlen];
+      row_band<DT>(in, L, P, grad, lds, __builtin_amdgcn_readfirstlane(bd.x), __builtin_amdgcn_readfirstlane(bd.y), w,
+                   lane, cur_b);
+    }
+    __syncthreads();
+  }
+}
+
+// LDS words per row wave: class sums, class bitmap and its prefix counts
+int64_t stream_words(const Layout& L) { return L.C_stride + 2 * L.Dw; }
+
+size_t stream_lds(const Layout& L) {
+  return ((sizeof(Shared) + 15) & ~size_t(15)) + sizeof(uint32_t) * kStreamWaves * (size_t)stream_words(L);
 }
 
 }  // namespace
@@ -478,6 +601,33 @@ hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, i
   // at most one workgroup (a segment of four waves, one per SIMD) per compute unit
   chain_workers<<<cus > 0 ? cus : 256, kThreads, kChainReserve, s>>>(in, L, P, group, store ? 1 : 0);
   return hipGetLastError();
+}
+
+// The streamed pipeline takes the 16-bit and float32 inputs of batches whose row waves' LDS fits a
+// compute unit beside the recursion rings and whose band queue one workgroup builds quickly.
+bool stream_fits(const Inputs& in, const Layout& L) {
+  return in.dtype != kF64 && L.B > 0 && L.B <= 2048 && L.T_total > 0 && L.D > 0 && stream_lds(L) <= 150 * 1024;
+}
+
+hipError_t launch_stream(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s) {
+  if (!stream_fits(in, L)) return hipErrorInvalidValue;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  // at least 96 KB: one workgroup per compute unit, so a recursion workgroup is alone on its unit
+  const size_t lds = std::max(stream_lds(L), (size_t)96 * 1024);
+  const int per_wave = static_cast<int>(stream_words(L));
+  auto launch = [&](auto kernel) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (err != hipSuccess) return err;
+    kernel<<<cus > 0 ? cus : 256, 64 * kStreamWaves, lds, s>>>(in, L, P, grad_out, per_wave);
+    return hipGetLastError();
+  };
+  if (in.dtype == kF32) return launch(&stream_workers<kF32>);
+  if (in.dtype == kF16) return launch(&stream_workers<kF16>);
+  return launch(&stream_workers<kBF16>);
 }
 
 }  // namespace pctc

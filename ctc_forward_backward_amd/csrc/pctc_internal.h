@@ -59,7 +59,7 @@ struct Layout {
   int64_t Dw;        // 32-bit words of a class bitmap: ceil(D / 32)
   int64_t C_stride;  // floats per row of the compact class sums (>= Umax + 1)
   size_t off_cbits, off_cpref, off_dmap, off_meta, off_lab, off_rowmap, off_rowoff, off_E, off_Eb, off_AB, off_nll, off_llb, off_lsh, off_w, off_post, off_order, off_cum, off_ring,
-      off_sig, off_items, off_ctl, total;
+      off_sig, off_items, off_ctl, off_prog, off_bands, total;
 };
 
 // Utterances are sorted by frame count (longest first) and cut into up to kMaxGroups groups of
@@ -85,9 +85,18 @@ struct GroupQ {
 struct ChainCtl {
   int err;      // non-zero: a block gave up waiting for its neighbour (results unspecified)
   int ngroups;
-  int pad[6];
+  int nbands;   // streamed pipeline: row bands queued after group 0's recursion segments
+  int pad[5];
   GroupQ g[kMaxGroups];
 };
+
+// Streamed pipeline: the rows of an utterance are handed out in bands of up to 2 kBand rows, band k
+// holding the frames t whose later-finished recursion step max(t, T-1-t) lies in
+// [T/2 + k kBand, T/2 + (k+1) kBand): a band can be formed as soon as both recursions have passed
+// its last such step, so the bands of an utterance become ready from the middle frames outwards.
+constexpr int kBand = 16;
+// workgroup of the streamed pipeline: four recursion waves (one per SIMD), or sixteen row waves
+constexpr int kStreamWaves = 16;
 
 Layout make_layout(int64_t T_total, int64_t D, int64_t B, int64_t Umax);
 
@@ -117,6 +126,11 @@ struct Pointers {
   int* cpref;       // (B, Dw) number of classes present in the words before each word
   int* dmap;        // (B, Umax + 1) rank among the present classes of lab[j]
   float* post;      // (T_total, C_stride) per row: the class sums times w / z, by class rank
+  // streamed pipeline: per (utterance, direction) the recursion steps whose states every block has
+  // stored where any compute unit sees them, and the queue of row bands (utterance, band), readiest
+  // first
+  int* prog;        // (2 B)
+  int2* bands;      // (T_total / kBand + 2 B + 1): at most ceil(ceil(T/2) / kBand) <= T/64 + 2 per utterance
 };
 
 Pointers carve(void* workspace, const Layout& L);
@@ -416,6 +430,11 @@ hipError_t launch_weights(const Inputs& in, const Layout& L, const Pointers& P, 
 hipError_t launch_classes(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
 hipError_t launch_posteriors(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s);
 hipError_t launch_dense(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, int group, hipStream_t s);
+// streamed pipeline (one group): the queue of row bands, then one persistent launch running the
+// recursions and, as their frames become ready, the posteriors and gradient rows
+bool stream_fits(const Inputs& in, const Layout& L);
+hipError_t launch_bands(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
+hipError_t launch_stream(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s);
 // zero gradient rows owned by no utterance
 hipError_t launch_gaps(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s);
 hipError_t launch_reduce(const float* losses, const void* target_lengths, bool i64, int64_t B, int reduction, float* out,

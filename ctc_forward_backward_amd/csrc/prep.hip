@@ -337,6 +337,62 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
   }
 }
 
+// Streamed pipeline: the queue of row bands (one workgroup).  Band k of utterance b (T frames) holds
+// the frames whose later recursion step max(t, T-1-t) lies in [T/2 + k kBand, T/2 + (k+1) kBand), and
+// is ready once both recursions have stored min(T/2 + (k+1) kBand, T) steps.  The bands are queued
+// by that step, ties by utterance: each band's place is counted directly (for every utterance, the
+// number of its bands that are readier), so no sort is needed.  Also clears the progress words.
+__device__ __forceinline__ int bands_of(int T) { return T > 0 ? ((T + 1) / 2 + kBand - 1) / kBand : 0; }
+
+// bands of an utterance with T frames that become ready before step `key`
+__device__ __forceinline__ int bands_before(int T, int key) {
+  if (T <= 0) return 0;
+  const int n = bands_of(T);
+  if (key > T) return n;
+  const int x = key - T / 2;
+  if (x <= 0) return 0;
+  return min(max((x + kBand - 1) / kBand - 1, 0), n);
+}
+
+__global__ void __launch_bounds__(1024) bands_kernel(Layout L, Pointers P) {
+  extern __shared__ int bsh[];  // T (B), then the first band of each utterance (B + 1)
+  const int B = static_cast<int>(L.B);
+  const int tid = threadIdx.x, nt = blockDim.x;
+  int* sT = bsh;
+  int* first = bsh + B;
+  for (int b = tid; b < B; b += nt) sT[b] = P.meta[b].T;
+  for (int i = tid; i < 2 * B; i += nt) P.prog[i] = 0;
+  __syncthreads();
+  if (tid == 0) {
+    int n = 0;
+    for (int b = 0; b < B; ++b) {
+      first[b] = n;
+      n += bands_of(sT[b]);
+    }
+    first[B] = n;
+    P.ctl->nbands = n;
+  }
+  __syncthreads();
+  const int N = first[B];
+  for (int i = tid; i < N; i += nt) {
+    int lo = 0, hi = B - 1;  // the utterance whose bands hold entry i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (first[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    const int b = lo, k = i - first[b], T = sT[b];
+    const int key = min(T / 2 + (k + 1) * kBand, T);
+    int rank = 0;
+    for (int c = 0; c < B; ++c) {
+      const int before = bands_before(sT[c], key);
+      rank += before;
+      if (c < b) rank += bands_before(sT[c], key + 1) - before;  // a band of c ready at the same step
+    }
+    P.bands[rank] = make_int2(b, k);
+  }
+}
+
 int grid_for(int64_t n, int threads) {
   int64_t g = (n + threads - 1) / threads;
   if (g > 4096) g = 4096;
@@ -402,6 +458,19 @@ hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P,
     if (e != hipSuccess) return e;
   }
   schedule_kernel<<<1, 1024, lds, s>>>(L, P, sort, groups);
+  return hipGetLastError();
+}
+
+hipError_t launch_bands(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {
+  (void)in;
+  if (L.B == 0) return hipGetLastError();
+  const size_t lds = sizeof(int) * (2 * (size_t)L.B + 1);
+  if (lds > 48 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bands_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  bands_kernel<<<1, 1024, lds, s>>>(L, P);
   return hipGetLastError();
 }
 

@@ -115,6 +115,93 @@ __device__ __forceinline__ void posterior_row(const Layout& L, const Pointers& P
   for (int i = lane; i <= U; i += 64) out[i] = acc[i] * scale;
 }
 
+// Streamed pipeline: the posteriors of row r of utterance b while the recursions may still be running
+// (the band scheduler has seen both pass this frame).  The likelihood is not known yet, so the
+// exponent reference is an integer found on the way: the first batch of blocks with mass sets it at
+// its largest term, a later batch with a larger term raises it and scales the sums so far down.  The
+// block offsets are read with device-coherent loads: a chunk's offset shares its cache line with
+// offsets of later chunks, which may be stored after this line was cached.  Leaves the row's class
+// sums times w / z in acc (U+1 floats, by class rank); false when the frame carries no mass (the
+// utterance has no alignment).
+__device__ __forceinline__ bool posterior_stream(const Layout& L, const Pointers& P, float* acc, int64_t r, int b,
+                                                 float w, int lane) {
+  const int64_t TT = L.T_total, Gm = L.Gmax;
+  const Meta m = P.meta[b];
+  const int U = m.U, G = (U + 64) >> 6;
+  const int64_t start = m.start, T = m.T;
+  const int64_t sa = r - start, sb = start + T - 1 - r;
+  const int64_t rowa = sa == 0 ? -1 : start + 1 + ((sa - 1) / kChunk) * kChunk;
+  const int64_t rowb = sb == 0 ? -1 : start + T - 1 - (1 + ((sb - 1) / kChunk) * kChunk);
+  auto sig = [&](int64_t i) { return __hip_atomic_load(P.sig + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+  auto offA = [&](int j) { return rowa < 0 ? 0 : sig(j * TT + rowa); };
+  auto offB = [&](int j) { return rowb < 0 ? 0 : sig((Gm + j) * TT + rowb); };
+  const int* dmap = P.dmap + (int64_t)b * (L.Umax + 1);
+  for (int i = lane; i <= U; i += 64) acc[i] = 0.0f;
+
+  int ref = offA(0) + offB(0);
+  bool have = false;
+  float z = 0.0f, bsum = 0.0f;
+  for (int j0 = 0; j0 < G; j0 += kBlocks) {
+    float x0[kBlocks], x1[kBlocks];
+    int d1[kBlocks];
+#pragma unroll
+    for (int u = 0; u < kBlocks; ++u) {
+      const int j = j0 + u, k = 64 * j + lane;
+      x0[u] = x1[u] = kNeg;
+      d1[u] = 0;
+      if (j < G) {
+        const int oa = offA(j), ob0 = offB(j);
+        const int ob1 = lane < 63 ? ob0 : (j + 1 < G ? offB(j + 1) : ob0);
+        const int64_t rb = ((Gm + j) * TT + r) * 128;
+        if (k <= U) {
+          const float2 a = *reinterpret_cast<const float2*>(P.AB + ((int64_t)j * TT + r) * 128 + 2 * lane);
+          x0[u] = a.x + P.AB[rb + 2 * lane + 1] + static_cast<float>(oa + ob0 - ref);
+          if (k < U) {
+            x1[u] = a.y + P.AB[lane < 63 ? rb + 2 * lane + 2 : rb + TT * 128] + static_cast<float>(oa + ob1 - ref);
+            d1[u] = dmap[k + 1];
+          }
+        }
+      }
+    }
+    float mx = kNeg;
+#pragma unroll
+    for (int u = 0; u < kBlocks; ++u) mx = fmaxf(mx, fmaxf(x0[u], x1[u]));
+    mx = wave_max(mx);
+    if (mx > kNegHalf && (!have || mx > 0.0f)) {  // wave-uniform
+      const float sh = floorf(mx);
+      if (have) {
+        const float sc = exp2_fast(-sh);
+        z *= sc;
+        bsum *= sc;
+        for (int i = lane; i <= U; i += 64) acc[i] *= sc;
+      }
+      ref += static_cast<int>(sh);
+      have = true;
+#pragma unroll
+      for (int u = 0; u < kBlocks; ++u) {
+        x0[u] -= sh;
+        x1[u] -= sh;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBlocks; ++u) {
+      const int k = 64 * (j0 + u) + lane;
+      const float p0 = k <= U ? exp2_fast(fminf(x0[u], 64.0f)) : 0.0f;
+      const float p1 = k < U ? exp2_fast(fminf(x1[u], 64.0f)) : 0.0f;
+      z += p0 + p1;
+      bsum += p0;
+      if (k < U) atomicAdd(&acc[d1[u]], p1);
+    }
+  }
+  z = wave_sum(z);
+  bsum = wave_sum(bsum);
+  if (lane == 0) atomicAdd(&acc[dmap[0]], bsum);
+  if (!(z > 0.0f)) return false;
+  const float scale = w / z;
+  for (int i = lane; i <= U; i += 64) acc[i] *= scale;
+  return true;
+}
+
 // row r of a dead utterance (zero weight: 0, no alignment or NaN: NaN) or of no utterance (0)
 template <int DT>
 __device__ __forceinline__ void fill_row(const Layout& L, void* grad, int64_t r, float fill, int lane) {
@@ -131,7 +218,8 @@ __device__ __forceinline__ void fill_row(const Layout& L, void* grad, int64_t r,
 // gradient row r of live utterance b (weight w), its class sums taken from P.post.  lds: this
 // wave's words, the class sums (C_stride) then the class bitmap (Dw) and its prefix counts (Dw);
 // cur_b: the utterance whose bitmap the LDS holds (updated here).
-template <int DT>
+// SUMS_IN_LDS: the class sums are already in the wave's LDS (streamed pipeline), not in P.post.
+template <int DT, bool SUMS_IN_LDS = false>
 __device__ __forceinline__ void dense_row(const Inputs& in, const Layout& L, const Pointers& P, void* grad,
                                           uint32_t* lds, int64_t r, int b, float w, int lane, int& cur_b) {
   const int Dw = static_cast<int>(L.Dw);
@@ -153,8 +241,10 @@ __device__ __forceinline__ void dense_row(const Inputs& in, const Layout& L, con
   const int U = P.meta[b].U;
   const float* pr = P.post + r * L.C_stride;
   float pv[kPost];
+  if (!SUMS_IN_LDS) {
 #pragma unroll
-  for (int k = 0; k < kPost; ++k) pv[k] = pr[min(lane + 64 * k, U)];
+    for (int k = 0; k < kPost; ++k) pv[k] = pr[min(lane + 64 * k, U)];
+  }
   if (b != cur_b) {  // this utterance's class bitmap and prefix counts into the wave's LDS
     const uint32_t* gb = P.cbits + (int64_t)b * Dw;
     const int* gp = P.cpref + (int64_t)b * Dw;
@@ -165,10 +255,12 @@ __device__ __forceinline__ void dense_row(const Inputs& in, const Layout& L, con
     cur_b = b;
   }
   // LDS operations of one wave complete in order: these writes precede every read below
+  if (!SUMS_IN_LDS) {
 #pragma unroll
-  for (int k = 0; k < kPost; ++k)
-    if (lane + 64 * k <= U) acc[lane + 64 * k] = pv[k];
-  for (int i = lane + 64 * kPost; i <= U; i += 64) acc[i] = pr[i];  // long targets
+    for (int k = 0; k < kPost; ++k)
+      if (lane + 64 * k <= U) acc[lane + 64 * k] = pv[k];
+    for (int i = lane + 64 * kPost; i <= U; i += 64) acc[i] = pr[i];  // long targets
+  }
 
   // stream the row once: w * exp(lp) minus the class posterior at the columns that carry one.
   // The classes of an aligned chunk of 8 columns are consecutive in rank order, so one rank per

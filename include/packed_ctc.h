@@ -65,6 +65,10 @@ extern "C" {
 #define PCTC_ERR_ARG 8                /* a required pointer is NULL, or an unknown flag / reduction */
 #define PCTC_ERR_LIMIT 9              /* beyond what this build supports (see packed_ctc_limits) */
 
+/* Pipelines of a packed_ctc_loss call that forms the gradient (packed_ctc_set_pipeline). */
+#define PCTC_PIPELINE_GROUPED 0   /* length-sorted groups on concurrent streams, rows after each group's recursions */
+#define PCTC_PIPELINE_STREAMED 1  /* one persistent launch: rows formed as the recursions pass them (default) */
+
 /*
  * Bytes of device workspace packed_ctc_loss needs for T_total frames, D classes, B utterances and
  * target lengths up to max_target_length.  Returns 0 for negative arguments.
@@ -182,6 +186,25 @@ const char* packed_ctc_last_error(void);
 
 /* Library version string. */
 const char* packed_ctc_version(void);
+
+/*
+ * Process-wide choice of pipeline for packed_ctc_loss calls with a gradient; both compute the same
+ * losses and gradient rows (the page's `_alpha_kernel` / `_beta_grad_kernel` split, NVIDIA-NeMo/Speech
+ * pull request "feat(asr): native CTC loss kernel over sequence-packed log probabilities", leaves the
+ * order of the work open).
+ *   PCTC_PIPELINE_STREAMED (default): after the label gather, one persistent launch runs the alpha
+ *     and beta recursions and hands out each utterance's rows in bands as soon as both recursions
+ *     have passed them (middle frames first), so posteriors and gradient rows stream beside the
+ *     recursions.  Used for float32, bfloat16 and float16 inputs of up to 2048 utterances whose
+ *     per-wave LDS (class sums, class bitmap) fits; other calls take the grouped pipeline.
+ *   PCTC_PIPELINE_GROUPED: utterances sorted by frame count and cut into up to three groups on
+ *     concurrent streams; each group forms its rows after its recursions end.
+ * Loss-only calls and the split forward / backward entry points do not depend on it.
+ * packed_ctc_set_pipeline returns PCTC_OK or PCTC_ERR_ARG (unknown value); packed_ctc_pipeline returns
+ * the current choice.  Calls already enqueued are not affected.
+ */
+int packed_ctc_set_pipeline(int pipeline);
+int packed_ctc_pipeline(void);
 
 /*
  * Measurement hook.  While enabled, packed_ctc_loss records a HIP event before and after each of

@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     for n in ("packed_ctc_loss", "packed_ctc_reduce", "packed_ctc_workspace_size", "packed_ctc_last_error",
               "packed_ctc_max_target_length", "packed_ctc_limits", "packed_ctc_version",
               "packed_ctc_set_phase_timing", "packed_ctc_phase_times", "packed_ctc_workspace_status",
-              "packed_ctc_forward", "packed_ctc_backward", "hmm_forward_loglik"):
+              "packed_ctc_forward", "packed_ctc_backward", "hmm_forward_loglik", "packed_ctc_set_pipeline",
+              "packed_ctc_pipeline"):
         assert n in names
 
 
@@ -195,3 +196,25 @@ def test_hmm_host_checks(kw, code, needle):
     rc = lib.hmm_forward_loglik(d, d, d, d, a["i64"], a["B"], a["T"], a["S"], a["O"], a["out"], None)
     assert rc == code
     assert needle in lib.packed_ctc_last_error().decode()
+
+
+def test_pipeline_switch():
+    """The pipeline choice is host state only: set, read back, unknown values rejected."""
+    src = open(HEADER).read()
+    codes = dict(re.findall(r"#define (PCTC_PIPELINE_\w+)\s+(\d+)", src))
+    assert {k: int(v) for k, v in codes.items()} == {"PCTC_PIPELINE_GROUPED": 0, "PCTC_PIPELINE_STREAMED": 1}
+    lib = api._load()
+    before = api.pipeline()
+    assert before == "streamed"  # the default
+    try:
+        api.set_pipeline("grouped")
+        assert api.pipeline() == "grouped" and lib.packed_ctc_pipeline() == 0
+        api.set_pipeline("streamed")
+        assert lib.packed_ctc_pipeline() == 1
+        assert lib.packed_ctc_set_pipeline(7) == api.ERR_ARG
+        assert "unknown pipeline" in lib.packed_ctc_last_error().decode()
+        assert api.pipeline() == "streamed"
+        with pytest.raises(ValueError):
+            api.set_pipeline("fast")
+    finally:
+        api.set_pipeline(before)

@@ -25,14 +25,18 @@ def _say(*a):
     print(*a, flush=True)
 
 
-@pytest.fixture(scope="module")
-def api():
+@pytest.fixture(scope="module", params=["streamed", "grouped"])
+def api(request):
+    """The binding, with the loss + gradient calls of the module on one pipeline, then the other."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from ctc_forward_backward_amd import api as _api
 
     _api._load()
-    return _api
+    _api.set_pipeline(request.param)
+    _say(f"pipeline: {request.param}")
+    yield _api
+    _api.set_pipeline("streamed")
 
 
 def run_gpu(api, batch, *, reduction=None, grad_scale=None, need_grad=True, max_target_length=None,

@@ -413,10 +413,15 @@ __device__ __forceinline__ float utterance_weight(const Inputs& in, int64_t B, i
   return static_cast<float>(w);
 }
 
-hipError_t launch_prep(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
-hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s);
+// setup (streamed pipeline): also clears the recursion rings and forms the class maps
+hipError_t launch_prep(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s, bool setup = false);
+// gaps: when given (the gradient), rows owned by no utterance are zeroed in the same launch
+hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s,
+                         void* gaps = nullptr);
 // sorts the utterances and cuts them into `groups` groups (see GroupQ)
-hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P, int groups, hipStream_t s);
+// setup (streamed pipeline, one group): the rings are already clear; also builds the row-band queue
+hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P, int groups, hipStream_t s,
+                           bool setup = false);
 // dense log-space HMM forward (hmm.hip): one log-likelihood per observation sequence
 hipError_t launch_hmm_forward(const float* log_init, const float* log_trans, const float* log_emit, const void* obs,
                               int obs_i64, int64_t B, int64_t T, int S, int O, float* out, hipStream_t s);
@@ -433,7 +438,6 @@ hipError_t launch_dense(const Inputs& in, const Layout& L, const Pointers& P, vo
 // streamed pipeline (one group): the queue of row bands, then one persistent launch running the
 // recursions and, as their frames become ready, the posteriors and gradient rows
 bool stream_fits(const Inputs& in, const Layout& L);
-hipError_t launch_bands(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
 hipError_t launch_stream(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s);
 // zero gradient rows owned by no utterance
 hipError_t launch_gaps(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s);

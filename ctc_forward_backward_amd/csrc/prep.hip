@@ -6,7 +6,7 @@
 // classes, computed in float32), `_PackedCTCLoss.forward` (zero_infinity on the loss) and
 // `_beta_grad_kernel` (the gradient scale, zero under zero_infinity for an infinite loss); `ctc.py`
 // `forward_packed` (sum, and the mean of each loss over its clamped target length, then the batch mean).
-#include "pctc_internal.h"
+#include "rows.h"
 
 namespace pctc {
 
@@ -16,13 +16,22 @@ __global__ void fill_i32_kernel(int* p, int64_t n, int v) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
+// two fills in one launch (the row map, the recursion rings)
+__global__ void fill2_i32_kernel(int* p, int64_t n, int v, int* q, int64_t m, int u) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < m; i += stride) q[i] = u;
+}
+
 __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0u;
 }
 
 // One workgroup per utterance: clamp the metadata so that every later access stays in bounds,
 // write the U+1 distinct class ids of the extended label sequence, claim the utterance's rows.
-__global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers P) {
+__device__ __forceinline__ void class_maps(const Layout& L, const Pointers& P, int b, uint32_t* cw, int* wsum);
+
+__global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers P, int classes) {
   const int b = blockIdx.x;
   __shared__ Meta m;
   if (threadIdx.x == 0) {
@@ -58,6 +67,12 @@ __global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers
     lab[j] = static_cast<int>(c);
   }
   for (int t = threadIdx.x; t < mm.T; t += blockDim.x) P.rowmap[mm.start + t] = b;
+  if (classes) {  // the class maps of this utterance (its labels were written above, by this workgroup)
+    extern __shared__ uint32_t pcw[];
+    __shared__ int wsum[4];
+    __syncthreads();
+    class_maps(L, P, b, pcw, wsum);
+  }
 }
 
 // One wave per owned row: the log2 emissions of the row at the utterance's U+1 label columns,
@@ -77,7 +92,7 @@ __device__ __forceinline__ float ld1(const void* p, int64_t i) {
 }
 
 template <int DT>
-__global__ void __launch_bounds__(256) gather_kernel(Inputs in, Layout L, Pointers P, int group) {
+__global__ void __launch_bounds__(256) gather_kernel(Inputs in, Layout L, Pointers P, int group, void* gaps) {
   const int lane = threadIdx.x & 63;
   const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int64_t j0, j1;
@@ -136,16 +151,19 @@ __global__ void __launch_bounds__(256) gather_kernel(Inputs in, Layout L, Pointe
     }
     if (nan) atomicOr(&P.meta[b].flags, 1);
   });
+  if (gaps) {  // streamed pipeline: rows owned by no utterance get a zero gradient here
+    const int64_t waves = (int64_t)gridDim.x * 4;
+    for (int64_t r = wid; r < L.T_total; r += waves)
+      if (__builtin_amdgcn_readfirstlane(P.rowmap[r]) < 0) rows::fill_row<DT>(L, gaps, r, 0.0f, lane);
+  }
 }
 
-// One workgroup per utterance: the bitmap of the classes its extended labels use (the blank and
+// Per utterance (one workgroup): the bitmap of the classes its extended labels use (the blank and
 // its labels), the number of classes before each bitmap word, and for each label index j the rank
 // of lab[j] among the present classes.  The gradient rows add each class's posterior at its
-// column through these ranks.
-__global__ void __launch_bounds__(256) classes_kernel(Layout L, Pointers P) {
-  extern __shared__ uint32_t cw[];  // Dw bitmap words, then Dw prefix counts
-  __shared__ int wsum[4];
-  const int b = blockIdx.x, tid = threadIdx.x;
+// column through these ranks.  cw: 2 Dw words of LDS.
+__device__ __forceinline__ void class_maps(const Layout& L, const Pointers& P, int b, uint32_t* cw, int* wsum) {
+  const int tid = threadIdx.x;
   const int Dw = static_cast<int>(L.Dw);
   const int U = P.meta[b].U;
   const int* lab = P.lab + (int64_t)b * (L.Umax + 1);
@@ -188,6 +206,12 @@ __global__ void __launch_bounds__(256) classes_kernel(Layout L, Pointers P) {
     const int c = lab[j], wi = c >> 5;
     dmap[j] = static_cast<int>(cw[Dw + wi]) + __builtin_popcount(cw[wi] & ((1u << (c & 31)) - 1u));
   }
+}
+
+__global__ void __launch_bounds__(256) classes_kernel(Layout L, Pointers P) {
+  extern __shared__ uint32_t cw[];  // Dw bitmap words, then Dw prefix counts
+  __shared__ int wsum[4];
+  class_maps(L, P, blockIdx.x, cw, wsum);
 }
 
 // Losses after zero_infinity, gradient weights and the sum / mean reduction (one workgroup,
@@ -251,8 +275,10 @@ __global__ void __launch_bounds__(256) reduce_kernel(const float* losses, const 
 // segments in producer order (last segment first).  A segment only ever waits on its producer,
 // which sits earlier in the queue, so segments claimed in queue order can always finish.
 // Frameless utterances get their loss here.
-__global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, int sort, int groups) {
-  extern __shared__ int sh[];  // sort ? [T (B) | order (B) | U (B)] : unused
+__device__ void build_bands(const Layout& L, const Pointers& P, int* sT, int* first);
+
+__global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, int sort, int groups, int bands) {
+  extern __shared__ int sh[];  // sort ? [T (B) | order (B) | U (B) | bands: first band (B + 1)] : unused
   const int B = static_cast<int>(L.B);
   const int tid = threadIdx.x, nt = blockDim.x;
   if (sort) {
@@ -335,6 +361,10 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
     P.ctl->err = 0;
     P.ctl->ngroups = groups;
   }
+  if (bands) {  // streamed pipeline (sorted, one group): the queue of row bands
+    __syncthreads();
+    build_bands(L, P, sh, sh + 3 * B);
+  }
 }
 
 // Streamed pipeline: the queue of row bands (one workgroup).  Band k of utterance b (T frames) holds
@@ -354,15 +384,11 @@ __device__ __forceinline__ int bands_before(int T, int key) {
   return min(max((x + kBand - 1) / kBand - 1, 0), n);
 }
 
-__global__ void __launch_bounds__(1024) bands_kernel(Layout L, Pointers P) {
-  extern __shared__ int bsh[];  // T (B), then the first band of each utterance (B + 1)
+// (one workgroup) sT: the frame counts (LDS, B); first: B + 1 words of LDS
+__device__ void build_bands(const Layout& L, const Pointers& P, int* sT, int* first) {
   const int B = static_cast<int>(L.B);
   const int tid = threadIdx.x, nt = blockDim.x;
-  int* sT = bsh;
-  int* first = bsh + B;
-  for (int b = tid; b < B; b += nt) sT[b] = P.meta[b].T;
   for (int i = tid; i < 2 * B; i += nt) P.prog[i] = 0;
-  __syncthreads();
   if (tid == 0) {
     int n = 0;
     for (int b = 0; b < B; ++b) {
@@ -401,15 +427,26 @@ int grid_for(int64_t n, int threads) {
 
 }  // namespace
 
-hipError_t launch_prep(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {
-  if (L.T_total > 0) {
-    fill_i32_kernel<<<grid_for(L.T_total, 256), 256, 0, s>>>(P.rowmap, L.T_total, -1);
+hipError_t launch_prep(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s, bool setup) {
+  // setup (streamed pipeline): the recursion rings are cleared here too (one fill launch) and the class
+  // maps are formed by the prep workgroups
+  const int64_t ring_words = setup ? 2 * 2 * L.Gmax * L.T_total : 0;
+  if (L.T_total > 0 || ring_words > 0)
+    fill2_i32_kernel<<<grid_for(std::max<int64_t>(L.T_total, ring_words), 256), 256, 0, s>>>(
+        P.rowmap, L.T_total, -1, reinterpret_cast<int*>(P.ring), ring_words, 0);
+  if (L.B > 0) {
+    const size_t lds = setup ? 2 * sizeof(uint32_t) * (size_t)L.Dw : 0;
+    if (lds > 48 * 1024) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+    }
+    prep_kernel<<<static_cast<unsigned>(L.B), 256, lds, s>>>(in, L, P, setup ? 1 : 0);
   }
-  if (L.B > 0) prep_kernel<<<static_cast<unsigned>(L.B), 256, 0, s>>>(in, L, P);
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s) {
+hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s, void* gaps) {
   if (L.T_total == 0 || L.B == 0) return hipGetLastError();
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -420,10 +457,10 @@ hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, i
   // reserves the rest of a compute unit's LDS)
   const int grid = 8 * (cus > 0 ? cus : 256);
   const size_t lds = kRowKernelLds;
-  if (in.dtype == kF32) gather_kernel<kF32><<<grid, 256, lds, s>>>(in, L, P, group);
-  else if (in.dtype == kF64) gather_kernel<kF64><<<grid, 256, lds, s>>>(in, L, P, group);
-  else if (in.dtype == kF16) gather_kernel<kF16><<<grid, 256, lds, s>>>(in, L, P, group);
-  else gather_kernel<kBF16><<<grid, 256, lds, s>>>(in, L, P, group);
+  if (in.dtype == kF32) gather_kernel<kF32><<<grid, 256, lds, s>>>(in, L, P, group, gaps);
+  else if (in.dtype == kF64) gather_kernel<kF64><<<grid, 256, lds, s>>>(in, L, P, group, gaps);
+  else if (in.dtype == kF16) gather_kernel<kF16><<<grid, 256, lds, s>>>(in, L, P, group, gaps);
+  else gather_kernel<kBF16><<<grid, 256, lds, s>>>(in, L, P, group, gaps);
   return hipGetLastError();
 }
 
@@ -440,7 +477,7 @@ hipError_t launch_classes(const Inputs& in, const Layout& L, const Pointers& P, 
   return hipGetLastError();
 }
 
-hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P, int groups, hipStream_t s) {
+hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P, int groups, hipStream_t s, bool setup) {
   (void)in;
   if (L.B == 0) {  // nothing to queue: the control words still start clean for the status read
     zero_u32_kernel<<<1, 256, 0, s>>>(reinterpret_cast<uint32_t*>(P.ctl), sizeof(ChainCtl) / 4);
@@ -448,29 +485,18 @@ hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P,
   }
   // every ring slot starts unwritten (zero: the written mark 0x80 of its high word is clear); a
   // block publishes (value, offset << 8 | 0x80 | tag) into it once
+  // (setup: cleared with the row map, in the prep launch)
   const int64_t words = 2 * 2 * L.Gmax * L.T_total;
-  if (words > 0) fill_i32_kernel<<<grid_for(words, 256), 256, 0, s>>>(reinterpret_cast<int*>(P.ring), words, 0);
+  if (words > 0 && !setup) fill_i32_kernel<<<grid_for(words, 256), 256, 0, s>>>(reinterpret_cast<int*>(P.ring), words, 0);
   const int sort = L.B <= 8192 ? 1 : 0;
-  const size_t lds = sort ? 3 * sizeof(int) * (size_t)L.B : 0;
+  if (setup && !sort) return hipErrorInvalidValue;  // the band queue needs the sorted frame counts
+  const size_t lds = sort ? sizeof(int) * (3 * (size_t)L.B + (setup ? (size_t)L.B + 1 : 0)) : 0;
   if (lds > 48 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&schedule_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  schedule_kernel<<<1, 1024, lds, s>>>(L, P, sort, groups);
-  return hipGetLastError();
-}
-
-hipError_t launch_bands(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {
-  (void)in;
-  if (L.B == 0) return hipGetLastError();
-  const size_t lds = sizeof(int) * (2 * (size_t)L.B + 1);
-  if (lds > 48 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bands_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-  }
-  bands_kernel<<<1, 1024, lds, s>>>(L, P);
+  schedule_kernel<<<1, 1024, lds, s>>>(L, P, sort, groups, setup ? 1 : 0);
   return hipGetLastError();
 }
 

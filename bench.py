@@ -5,10 +5,13 @@ the large-vocabulary batch: B=16 utterances, T_i uniform in [500, 3000], D=8193 
 U_i = round(T_i/6), float16 log probabilities, reduction mean.  Inputs are generated with a fixed
 seed and are resident in HBM before the timed region.
 
+The calls run on the streamed pipeline (one persistent launch for the recursions and the gradient
+rows) unless --pipeline grouped is given; the other pipeline is timed too, for context.
+
 Prints one JSON line with frames/s, the whole-call HBM rate over the counted bytes
 T_total * D * (2 bytes read + 2 bytes written), the per-kernel breakdown from HIP events recorded
-on each group's stream during a second pass of the same number of steps (the timed pass records
-no events of its own), the roofline of the dominant kernel, and the float64 CPU oracle timed on
+around each kernel during a second pass of the same number of steps (the timed pass records no
+events of its own), the roofline of the dominant kernel, and the float64 CPU oracle timed on
 this host's cores on the same batch.
 """
 
@@ -35,7 +38,7 @@ DTYPE_BYTES = {"f32": 4, "bf16": 2, "f16": 2}
 OPS_PER_STATE_STEP = 12
 
 
-PHASE_KERNELS = {"chains": "chain_workers", "dense": "dense_kernel", "gather": "gather_kernel"}
+PHASE_KERNELS = {"chains": "chain_workers", "dense": "dense_kernel", "gather": "gather_kernel", "stream": "stream_workers"}
 
 
 def kernel_sources_sha() -> str:
@@ -81,6 +84,11 @@ def parse():
                     choices=["tiny", "small", "asr_bpe", "large_vocab", "char_level"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU-baseline leg")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="only the warmup, timed and phase-timed steps (no call medians, other pipeline or HMM "
+                         "leg): the run a profiler traces")
+    ap.add_argument("--pipeline", default="streamed", choices=["streamed", "grouped"],
+                    help="pipeline of the timed calls (the other one is timed too, for context)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one device copy of 512 MiB (a known-size kernel for "
                          "scaling hardware byte counters)")
@@ -107,6 +115,7 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     lib = api._load()
+    api.set_pipeline(args.pipeline)
 
     b = W.make_workload(args.workload)
     T_total, D, B = b.T_total, b.D, b.B
@@ -232,57 +241,74 @@ def main():
         "roofline_rows": roofline_rows,
     }
 
-    # per-call medians with HIP events around single calls: warm (back to back) and cold (L2 and
-    # MALL flushed by writing a 512 MB buffer before each call); and the attainable rate, a 1 GB
-    # device-to-device copy
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    nmed = 20
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2 * nmed)]
-    for k, (e0, e1) in enumerate(evs):
-        if k >= nmed:
-            flush.fill_(k & 0xff)
-        e0.record(stream)
-        step()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    warm = sorted(e0.elapsed_time(e1) for e0, e1 in evs[:nmed])
-    cold = sorted(e0.elapsed_time(e1) for e0, e1 in evs[nmed:])
-    del flush
-    csrc_ = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    cdst_ = torch.empty_like(csrc_)
-    cdst_.copy_(csrc_)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(5):
+    if not args.profile_run:
+        # per-call medians with HIP events around single calls: warm (back to back) and cold (L2 and
+        # MALL flushed by writing a 512 MB buffer before each call); and the attainable rate, a 1 GB
+        # device-to-device copy
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        nmed = 20
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2 * nmed)]
+        for k, (e0, e1) in enumerate(evs):
+            if k >= nmed:
+                flush.fill_(k & 0xff)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        warm = sorted(e0.elapsed_time(e1) for e0, e1 in evs[:nmed])
+        cold = sorted(e0.elapsed_time(e1) for e0, e1 in evs[nmed:])
+        del flush
+        csrc_ = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cdst_ = torch.empty_like(csrc_)
         cdst_.copy_(csrc_)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del csrc_, cdst_
-    out["call_medians_ms"] = {"warm": warm[len(warm) // 2], "cold_l2_mall_flushed": cold[len(cold) // 2],
-                              "calls": nmed}
-    out["call_hbm"]["device_copy_gbps"] = copy_gbps
-    out["call_hbm"]["frac_of_device_copy"] = call_gbps / copy_gbps
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(5):
+            cdst_.copy_(csrc_)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = 5 * 2 * (1 << 30) / (c0.elapsed_time(c1) * 1e-3) / 1e9
+        del csrc_, cdst_
+        out["call_medians_ms"] = {"warm": warm[len(warm) // 2], "cold_l2_mall_flushed": cold[len(cold) // 2],
+                                  "calls": nmed, "pipeline": args.pipeline}
+        # the other pipeline, same calls (warm median), for context
+        other = "grouped" if args.pipeline == "streamed" else "streamed"
+        api.set_pipeline(other)
+        for _ in range(3):
+            step()
+        oth = []
+        for e0, e1 in evs[:nmed]:
+            e0.record(stream)
+            step()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        oth = sorted(e0.elapsed_time(e1) for e0, e1 in evs[:nmed])
+        api.set_pipeline(args.pipeline)
+        step()  # (the gradient left in grad is the timed pipeline's, for the parity check below)
+        torch.cuda.synchronize()
+        out["call_medians_ms"]["other_pipeline"] = {"pipeline": other, "warm": oth[len(oth) // 2]}
+        out["call_hbm"]["device_copy_gbps"] = copy_gbps
+        out["call_hbm"]["frac_of_device_copy"] = call_gbps / copy_gbps
 
-    # the second workload of the library: the dense HMM forward at the HMM page's size
-    # (S = 16 states, T = 128 frames, B = 64 sequences, O = 64 symbols), HIP events on the stream
-    hrng = np.random.default_rng(16)
-    hS, hT, hB, hO = 16, 128, 64, 64
-    h_in = [torch.from_numpy(hrng.normal(0, 1, size=sh).astype(np.float32)).to(dev) for sh in ((hS,), (hS, hS), (hS, hO))]
-    h_obs = torch.from_numpy(hrng.integers(0, hO, size=(hB, hT)).astype(np.int32)).to(dev)
-    for _ in range(5):
-        api.hmm_forward(*h_in, h_obs)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    hreps = 200
-    ev0.record(stream)
-    for _ in range(hreps):
-        api.hmm_forward(*h_in, h_obs)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    h_us = ev0.elapsed_time(ev1) * 1e3 / hreps
-    out["hmm_forward"] = {"workload": f"S={hS} T={hT} B={hB} O={hO} float32", "us_per_call": h_us,
-                          "sequences_per_s": hB / (h_us * 1e-6), "frames_per_s": hB * hT / (h_us * 1e-6),
-                          "bound": "latency of T dependent log-semiring matrix-vector steps"}
+        # the second workload of the library: the dense HMM forward at the HMM page's size
+        # (S = 16 states, T = 128 frames, B = 64 sequences, O = 64 symbols), HIP events on the stream
+        hrng = np.random.default_rng(16)
+        hS, hT, hB, hO = 16, 128, 64, 64
+        h_in = [torch.from_numpy(hrng.normal(0, 1, size=sh).astype(np.float32)).to(dev) for sh in ((hS,), (hS, hS), (hS, hO))]
+        h_obs = torch.from_numpy(hrng.integers(0, hO, size=(hB, hT)).astype(np.int32)).to(dev)
+        for _ in range(5):
+            api.hmm_forward(*h_in, h_obs)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        hreps = 200
+        ev0.record(stream)
+        for _ in range(hreps):
+            api.hmm_forward(*h_in, h_obs)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        h_us = ev0.elapsed_time(ev1) * 1e3 / hreps
+        out["hmm_forward"] = {"workload": f"S={hS} T={hT} B={hB} O={hO} float32", "us_per_call": h_us,
+                              "sequences_per_s": hB / (h_us * 1e-6), "frames_per_s": hB * hT / (h_us * 1e-6),
+                              "bound": "latency of T dependent log-semiring matrix-vector steps"}
 
     if args.copy_calibration:  # last device work of the run
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)

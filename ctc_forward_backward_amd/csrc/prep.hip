@@ -277,17 +277,63 @@ __global__ void __launch_bounds__(256) reduce_kernel(const float* losses, const 
 // Frameless utterances get their loss here.
 __device__ void build_bands(const Layout& L, const Pointers& P, int* sT, int* first);
 
+// exclusive prefix sum of a[0..n) in place, with a[n] = the total (one workgroup; every thread calls
+// it); wsum: blockDim / 64 words of LDS
+__device__ void block_exclusive_scan(int* a, int n, int* wsum) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int per = (n + nt - 1) / nt;
+  const int i0 = min(tid * per, n), i1 = min(i0 + per, n);
+  int s = 0;
+  for (int i = i0; i < i1; ++i) s += a[i];
+  const int lane = tid & 63, wave = tid >> 6;
+  int v = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  int run = v - s;
+  for (int k = 0; k < wave; ++k) run += wsum[k];
+  for (int i = i0; i < i1; ++i) {
+    const int x = a[i];
+    a[i] = run;
+    run += x;
+  }
+  if (tid == 0) {
+    int t = 0;
+    for (int k = 0; k < nt / 64; ++k) t += wsum[k];
+    a[n] = t;
+  }
+  __syncthreads();
+}
+
 __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, int sort, int groups, int bands) {
-  extern __shared__ int sh[];  // sort ? [T (B) | order (B) | U (B) | bands: first band (B + 1)] : unused
+  // sort ? [T (B) | order (B) | U (B) | rows before each sorted position (B + 1) | queue entries before
+  // each sorted position (B + 1) | bands: first band of each utterance (B + 1)] : unused
+  extern __shared__ int sh[];
+  __shared__ int wsum[16];
+  __shared__ int gfirst[kMaxGroups + 1];
   const int B = static_cast<int>(L.B);
   const int tid = threadIdx.x, nt = blockDim.x;
+  auto nseg_of = [](int U) { return (((U + 1 + 63) >> 6) + kSegWaves - 1) / kSegWaves; };
+  // group g ends where the groups so far hold the share of the rows below (each group at least one
+  // utterance); its segments in sorted order, each utterance's producers first.  With three
+  // groups (cut points measured on uniformly spread lengths): the longest recursions with about
+  // half the rows on the caller's stream, then the middle, then the short ones, whose gathers,
+  // recursions and rows all finish under the long recursions
+  const float share[kMaxGroups][kMaxGroups] = {{1.0f, 1.0f, 1.0f}, {0.15f, 1.0f, 1.0f}, {0.45f, 0.75f, 1.0f}};
   if (sort) {
     int* sT = sh;
     int* order = sh + B;
+    int* sU = sh + 2 * B;
+    int* cT = sh + 3 * B;
+    int* cS = sh + 4 * B + 1;
     for (int b = tid; b < B; b += nt) {
       const Meta m = P.meta[b];
       sT[b] = m.T;
-      sh[2 * B + b] = m.U;
+      sU[b] = m.U;
     }
     __syncthreads();
     for (int b = tid; b < B; b += nt) {
@@ -300,8 +346,107 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
       order[rank] = b;
     }
     __syncthreads();
+    // frames and queue entries per sorted position, then their prefix sums
+    for (int i = tid; i < B; i += nt) {
+      const int b = order[i];
+      cT[i] = sT[b];
+      cS[i] = sT[b] > 0 ? 2 * nseg_of(sU[b]) : 0;
+    }
+    __syncthreads();
+    block_exclusive_scan(cT, B, wsum);
+    block_exclusive_scan(cS, B, wsum);
+    if (tid == 0) {
+      // the cuts: group g takes positions [p0, p1), p1 the first position past p0 where the rows so far
+      // reach the group's share, at most B - (groups after it)
+      const int64_t total = cT[B];
+      int pos = 0;
+      for (int g = 0; g < kMaxGroups; ++g) {
+        GroupQ q{};
+        if (g < groups) {
+          const int p0 = pos, keep = groups - 1 - g;
+          int p1 = B;
+          if (g < groups - 1) {
+            const int64_t goal = static_cast<int64_t>(share[groups - 1][g] * (double)total);
+            int lo = p0 + 1, hi = B - keep;  // smallest p1 in [p0 + 1, B - keep] with cT[p1] >= goal
+            while (lo < hi) {
+              const int mid = (lo + hi) >> 1;
+              if ((int64_t)cT[mid] >= goal) hi = mid;
+              else lo = mid + 1;
+            }
+            p1 = lo;
+          }
+          q.itemoff = cS[p0];
+          q.qlen = cS[p1] - cS[p0];
+          q.first = p0;
+          q.count = p1 - p0;
+          q.nrows = cT[p1] - cT[p0];
+          gfirst[g] = p0;
+          pos = p1;
+        }
+        P.ctl->g[g] = q;
+      }
+      gfirst[groups] = B;
+      P.ctl->err = 0;
+      P.ctl->ngroups = groups;
+    }
+    __syncthreads();
+    for (int i = tid; i < B; i += nt) {
+      const int b = order[i];
+      P.order[i] = b;
+      int g = 0;
+      while (g + 1 < groups && gfirst[g + 1] <= i) ++g;
+      P.cum[i] = cT[i] - cT[gfirst[g]];
+      if (sT[b] == 0) continue;
+      const int nseg = nseg_of(sU[b]);
+      int n = cS[i];
+      for (int j = 0; j < nseg; ++j) {
+        P.items[n++] = ((2 * b) << 12) | j;
+        P.items[n++] = ((2 * b + 1) << 12) | (nseg - 1 - j);
+      }
+    }
+  } else {  // too many utterances to sort: identity order, serial (groups is 1 here)
+    for (int i = tid; i < B; i += nt) P.order[i] = i;
+    if (tid == 0) {
+      int64_t total = 0;
+      for (int i = 0; i < B; ++i) total += P.meta[i].T;
+      int n = 0, pos = 0;
+      int64_t done = 0;
+      for (int g = 0; g < kMaxGroups; ++g) {
+        GroupQ q{};
+        if (g < groups) {
+          const int p0 = pos;
+          const int64_t goal = g == groups - 1 ? total : static_cast<int64_t>(share[groups - 1][g] * (double)total);
+          int p1 = p0;
+          const int keep = groups - 1 - g;  // utterances to leave for the groups after this one
+          do {
+            done += P.meta[p1].T;
+            ++p1;
+          } while (p1 < B - keep && (done < goal || g == groups - 1));
+          q.itemoff = n;
+          q.first = p0;
+          q.count = p1 - p0;
+          int rows = 0;
+          for (int i = p0; i < p1; ++i) {
+            const Meta m = P.meta[i];
+            P.cum[i] = rows;
+            rows += m.T;
+            if (m.T == 0) continue;
+            const int nseg = nseg_of(m.U);
+            for (int j = 0; j < nseg; ++j) {
+              P.items[n++] = ((2 * i) << 12) | j;
+              P.items[n++] = ((2 * i + 1) << 12) | (nseg - 1 - j);
+            }
+          }
+          q.qlen = n - q.itemoff;
+          q.nrows = rows;
+          pos = p1;
+        }
+        P.ctl->g[g] = q;
+      }
+      P.ctl->err = 0;
+      P.ctl->ngroups = groups;
+    }
   }
-  for (int i = tid; i < B; i += nt) P.order[i] = sort ? sh[B + i] : i;
   for (int b = tid; b < B; b += nt) {
     const Meta m = P.meta[b];
     if (m.T == 0) {
@@ -309,61 +454,9 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
       P.llb[b] = m.U == 0 ? 0.0 : -(double)INFINITY;
     }
   }
-  if (tid == 0) {
-    // group g ends where the groups so far hold the share of the rows below (each group at least one
-    // utterance); its segments in sorted order, each utterance's producers first.  With three
-    // groups (cut points measured on uniformly spread lengths): the longest recursions with about
-    // half the rows on the caller's stream, then the middle, then the short ones, whose gathers,
-    // recursions and rows all finish under the long recursions
-    const float share[kMaxGroups][kMaxGroups] = {{1.0f, 1.0f, 1.0f}, {0.15f, 1.0f, 1.0f}, {0.45f, 0.75f, 1.0f}};
-    // frame and label counts from LDS when sorted (a serial walk over global memory would wait on
-    // every load)
-    auto Tat = [&](int b) { return sort ? sh[b] : P.meta[b].T; };
-    auto Uat = [&](int b) { return sort ? sh[2 * B + b] : P.meta[b].U; };
-    int64_t total = 0;
-    for (int i = 0; i < B; ++i) total += Tat(sort ? sh[B + i] : i);
-    int n = 0, pos = 0;
-    int64_t done = 0;
-    for (int g = 0; g < kMaxGroups; ++g) {
-      GroupQ q{};
-      if (g < groups) {
-        const int p0 = pos;
-        const int64_t goal = g == groups - 1 ? total : static_cast<int64_t>(share[groups - 1][g] * (double)total);
-        int p1 = p0;
-        const int keep = groups - 1 - g;  // utterances to leave for the groups after this one
-        do {
-          done += Tat(sort ? sh[B + p1] : p1);
-          ++p1;
-        } while (p1 < B - keep && (done < goal || g == groups - 1));
-        q.itemoff = n;
-        q.first = p0;
-        q.count = p1 - p0;
-        int rows = 0;
-        for (int i = p0; i < p1; ++i) {
-          const int b = sort ? sh[B + i] : i;
-          const int Tb = Tat(b), Ub = Uat(b);
-          P.cum[i] = rows;
-          rows += Tb;
-          if (Tb == 0) continue;
-          // segments of kSegWaves 64-pair blocks
-          const int nseg = (((Ub + 1 + 63) >> 6) + kSegWaves - 1) / kSegWaves;
-          for (int j = 0; j < nseg; ++j) {
-            P.items[n++] = ((2 * b) << 12) | j;
-            P.items[n++] = ((2 * b + 1) << 12) | (nseg - 1 - j);
-          }
-        }
-        q.qlen = n - q.itemoff;
-        q.nrows = rows;
-        pos = p1;
-      }
-      P.ctl->g[g] = q;
-    }
-    P.ctl->err = 0;
-    P.ctl->ngroups = groups;
-  }
   if (bands) {  // streamed pipeline (sorted, one group): the queue of row bands
     __syncthreads();
-    build_bands(L, P, sh, sh + 3 * B);
+    build_bands(L, P, sh, sh + 5 * B + 2);
   }
 }
 
@@ -388,18 +481,13 @@ __device__ __forceinline__ int bands_before(int T, int key) {
 __device__ void build_bands(const Layout& L, const Pointers& P, int* sT, int* first) {
   const int B = static_cast<int>(L.B);
   const int tid = threadIdx.x, nt = blockDim.x;
+  __shared__ int bsum[16];
   for (int i = tid; i < 2 * B; i += nt) P.prog[i] = 0;
-  if (tid == 0) {
-    int n = 0;
-    for (int b = 0; b < B; ++b) {
-      first[b] = n;
-      n += bands_of(sT[b]);
-    }
-    first[B] = n;
-    P.ctl->nbands = n;
-  }
+  for (int b = tid; b < B; b += nt) first[b] = bands_of(sT[b]);
   __syncthreads();
+  block_exclusive_scan(first, B, bsum);
   const int N = first[B];
+  if (tid == 0) P.ctl->nbands = N;
   for (int i = tid; i < N; i += nt) {
     int lo = 0, hi = B - 1;  // the utterance whose bands hold entry i
     while (lo < hi) {
@@ -490,7 +578,7 @@ hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P,
   if (words > 0 && !setup) fill_i32_kernel<<<grid_for(words, 256), 256, 0, s>>>(reinterpret_cast<int*>(P.ring), words, 0);
   const int sort = L.B <= 8192 ? 1 : 0;
   if (setup && !sort) return hipErrorInvalidValue;  // the band queue needs the sorted frame counts
-  const size_t lds = sort ? sizeof(int) * (3 * (size_t)L.B + (setup ? (size_t)L.B + 1 : 0)) : 0;
+  const size_t lds = sort ? sizeof(int) * (5 * (size_t)L.B + 2 + (setup ? (size_t)L.B + 1 : 0)) : 0;
   if (lds > 48 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&schedule_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));

@@ -275,7 +275,8 @@ __global__ void __launch_bounds__(256) reduce_kernel(const float* losses, const 
 // segments in producer order (last segment first).  A segment only ever waits on its producer,
 // which sits earlier in the queue, so segments claimed in queue order can always finish.
 // Frameless utterances get their loss here.
-__device__ void build_bands(const Layout& L, const Pointers& P, int* sT, int* first);
+constexpr int kBandBuckets = 4096;  // LDS buckets of 16 ready steps (a counting sort up to 65535 frames)
+__device__ void build_bands(const Layout& L, const Pointers& P, int* sT, int* first, int* hist, int nhist);
 
 // exclusive prefix sum of a[0..n) in place, with a[n] = the total (one workgroup; every thread calls
 // it); wsum: blockDim / 64 words of LDS
@@ -456,15 +457,14 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
   }
   if (bands) {  // streamed pipeline (sorted, one group): the queue of row bands
     __syncthreads();
-    build_bands(L, P, sh, sh + 5 * B + 2);
+    build_bands(L, P, sh, sh + 5 * B + 2, sh + 6 * B + 3, kBandBuckets);
   }
 }
 
-// Streamed pipeline: the queue of row bands (one workgroup).  Band k of utterance b (T frames) holds
-// the frames whose later recursion step max(t, T-1-t) lies in [T/2 + k kBand, T/2 + (k+1) kBand), and
-// is ready once both recursions have stored min(T/2 + (k+1) kBand, T) steps.  The bands are queued
-// by that step, ties by utterance: each band's place is counted directly (for every utterance, the
-// number of its bands that are readier), so no sort is needed.  Also clears the progress words.
+// Streamed pipeline: the queue of row bands (built by the schedule workgroup).  Band k of utterance b
+// (T frames) holds the frames whose later recursion step max(t, T-1-t) lies in
+// [T/2 + k kBand, T/2 + (k+1) kBand), and is ready once both recursions have stored
+// min(T/2 + (k+1) kBand, T) steps.  The bands are queued by that step.  Also clears the progress words.
 __device__ __forceinline__ int bands_of(int T) { return T > 0 ? ((T + 1) / 2 + kBand - 1) / kBand : 0; }
 
 // bands of an utterance with T frames that become ready before step `key`
@@ -478,25 +478,54 @@ __device__ __forceinline__ int bands_before(int T, int key) {
 }
 
 // (one workgroup) sT: the frame counts (LDS, B); first: B + 1 words of LDS
-__device__ void build_bands(const Layout& L, const Pointers& P, int* sT, int* first) {
+__device__ void build_bands(const Layout& L, const Pointers& P, int* sT, int* first, int* hist, int nhist) {
   const int B = static_cast<int>(L.B);
   const int tid = threadIdx.x, nt = blockDim.x;
   __shared__ int bsum[16];
+  __shared__ int tmax;
+  if (tid == 0) tmax = 0;
   for (int i = tid; i < 2 * B; i += nt) P.prog[i] = 0;
   for (int b = tid; b < B; b += nt) first[b] = bands_of(sT[b]);
   __syncthreads();
+  for (int b = tid; b < B; b += nt) atomicMax(&tmax, sT[b]);
   block_exclusive_scan(first, B, bsum);
   const int N = first[B];
   if (tid == 0) P.ctl->nbands = N;
-  for (int i = tid; i < N; i += nt) {
-    int lo = 0, hi = B - 1;  // the utterance whose bands hold entry i
+  auto band_of = [&](int i, int& b, int& k, int& key) {  // entry i: utterance, band, ready step
+    int lo = 0, hi = B - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (first[mid] <= i) lo = mid;
       else hi = mid - 1;
     }
-    const int b = lo, k = i - first[b], T = sT[b];
-    const int key = min(T / 2 + (k + 1) * kBand, T);
+    b = lo;
+    k = i - first[b];
+    key = min(sT[b] / 2 + (k + 1) * kBand, sT[b]);
+  };
+  const int nb = (tmax >> 4) + 1;  // buckets of 16 steps
+  if (nb <= nhist) {
+    // counting sort by 16-step bucket of the ready step; within a bucket, in order of arrival (bands
+    // ready within 16 steps of each other: the order only schedules, it changes no result)
+    for (int q = tid; q <= nb; q += nt) hist[q] = 0;
+    __syncthreads();
+    for (int i = tid; i < N; i += nt) {
+      int b, k, key;
+      band_of(i, b, k, key);
+      atomicAdd(&hist[key >> 4], 1);
+    }
+    __syncthreads();
+    block_exclusive_scan(hist, nb, bsum);
+    for (int i = tid; i < N; i += nt) {
+      int b, k, key;
+      band_of(i, b, k, key);
+      P.bands[atomicAdd(&hist[key >> 4], 1)] = make_int2(b, k);
+    }
+    return;
+  }
+  // longer utterances: the exact order by ready step, ties by utterance, each band's place counted
+  for (int i = tid; i < N; i += nt) {
+    int b, k, key;
+    band_of(i, b, k, key);
     int rank = 0;
     for (int c = 0; c < B; ++c) {
       const int before = bands_before(sT[c], key);
@@ -576,9 +605,10 @@ hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P,
   // (setup: cleared with the row map, in the prep launch)
   const int64_t words = 2 * 2 * L.Gmax * L.T_total;
   if (words > 0 && !setup) fill_i32_kernel<<<grid_for(words, 256), 256, 0, s>>>(reinterpret_cast<int*>(P.ring), words, 0);
-  const int sort = L.B <= 8192 ? 1 : 0;
+  const int sort = L.B <= 7168 ? 1 : 0;  // (the sorted path's LDS: 5 B words, at most 140 KB)
   if (setup && !sort) return hipErrorInvalidValue;  // the band queue needs the sorted frame counts
-  const size_t lds = sort ? sizeof(int) * (5 * (size_t)L.B + 2 + (setup ? (size_t)L.B + 1 : 0)) : 0;
+  // (setup: also the first band per utterance and the band buckets)
+  const size_t lds = sort ? sizeof(int) * (5 * (size_t)L.B + 2 + (setup ? (size_t)L.B + 1 + kBandBuckets + 1 : 0)) : 0;
   if (lds > 48 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&schedule_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));

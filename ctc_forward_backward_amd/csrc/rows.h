@@ -142,52 +142,60 @@ __device__ __forceinline__ bool posterior_stream(const Layout& L, const Pointers
   bool have = false;
   float z = 0.0f, bsum = 0.0f;
   for (int j0 = 0; j0 < G; j0 += kBlocks) {
-    float x0[kBlocks], x1[kBlocks];
-    int d1[kBlocks];
+    // a term's exponent is (alpha + beta) + (its blocks' offsets - ref): the sum of the stored values
+    // and the integer part are kept apart, so that the exponent is formed only after the reference
+    // has moved near the largest term (a long utterance's offsets reach 1e5, where float has no
+    // digits left for the fraction)
+    float s0[kBlocks], s1[kBlocks];
+    int c0[kBlocks], c1[kBlocks], d1[kBlocks];
 #pragma unroll
     for (int u = 0; u < kBlocks; ++u) {
       const int j = j0 + u, k = 64 * j + lane;
-      x0[u] = x1[u] = kNeg;
+      s0[u] = s1[u] = kNeg;
+      c0[u] = c1[u] = 0;
       d1[u] = 0;
       if (j < G) {
         const int oa = offA(j), ob0 = offB(j);
         const int ob1 = lane < 63 ? ob0 : (j + 1 < G ? offB(j + 1) : ob0);
         const int64_t rb = ((Gm + j) * TT + r) * 128;
+        c0[u] = oa + ob0 - ref;
+        c1[u] = oa + ob1 - ref;
         if (k <= U) {
           const float2 a = *reinterpret_cast<const float2*>(P.AB + ((int64_t)j * TT + r) * 128 + 2 * lane);
-          x0[u] = a.x + P.AB[rb + 2 * lane + 1] + static_cast<float>(oa + ob0 - ref);
+          s0[u] = a.x + P.AB[rb + 2 * lane + 1];
           if (k < U) {
-            x1[u] = a.y + P.AB[lane < 63 ? rb + 2 * lane + 2 : rb + TT * 128] + static_cast<float>(oa + ob1 - ref);
+            s1[u] = a.y + P.AB[lane < 63 ? rb + 2 * lane + 2 : rb + TT * 128];
             d1[u] = dmap[k + 1];
           }
         }
       }
     }
-    float mx = kNeg;
+    float mx = kNeg;  // (approximate: only its integer part is used)
 #pragma unroll
-    for (int u = 0; u < kBlocks; ++u) mx = fmaxf(mx, fmaxf(x0[u], x1[u]));
+    for (int u = 0; u < kBlocks; ++u)
+      mx = fmaxf(mx, fmaxf(s0[u] + static_cast<float>(c0[u]), s1[u] + static_cast<float>(c1[u])));
     mx = wave_max(mx);
     if (mx > kNegHalf && (!have || mx > 0.0f)) {  // wave-uniform
-      const float sh = floorf(mx);
+      const int sh = static_cast<int>(floorf(mx));
       if (have) {
-        const float sc = exp2_fast(-sh);
+        const float sc = exp2_fast(-static_cast<float>(sh));
         z *= sc;
         bsum *= sc;
         for (int i = lane; i <= U; i += 64) acc[i] *= sc;
       }
-      ref += static_cast<int>(sh);
+      ref += sh;
       have = true;
 #pragma unroll
       for (int u = 0; u < kBlocks; ++u) {
-        x0[u] -= sh;
-        x1[u] -= sh;
+        c0[u] -= sh;
+        c1[u] -= sh;
       }
     }
 #pragma unroll
     for (int u = 0; u < kBlocks; ++u) {
       const int k = 64 * (j0 + u) + lane;
-      const float p0 = k <= U ? exp2_fast(fminf(x0[u], 64.0f)) : 0.0f;
-      const float p1 = k < U ? exp2_fast(fminf(x1[u], 64.0f)) : 0.0f;
+      const float p0 = k <= U ? exp2_fast(fminf(s0[u] + static_cast<float>(c0[u]), 64.0f)) : 0.0f;
+      const float p1 = k < U ? exp2_fast(fminf(s1[u] + static_cast<float>(c1[u]), 64.0f)) : 0.0f;
       z += p0 + p1;
       bsum += p0;
       if (k < U) atomicAdd(&acc[d1[u]], p1);

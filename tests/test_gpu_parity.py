@@ -187,6 +187,20 @@ def test_long_targets_multiple_pairs_per_lane(api, oracle_mod):
     compare(run_gpu(api, b), oracle_mod.ctc_batch(b), torch.float32, "long targets")
 
 
+@pytest.mark.parametrize("B", [2048, 7200])
+def test_many_short_utterances(api, oracle_mod, B):
+    # 2048: the streamed pipeline's largest batch (4096 recursion segments, far more than compute
+    # units, so segments wait for free workgroups; the schedule's prefix sums and band queue at full
+    # size).  7200: more utterances than the schedule sorts (one group, utterance order)
+    _say(f"[gpu parity] {B} short utterances")
+    rng = np.random.default_rng(B)
+    lengths = [int(x) for x in rng.integers(1, 41, size=B)]
+    tl = [int(min(x, max(t // 2, 0))) for x, t in zip(rng.integers(0, 11, size=B), lengths)]
+    targets = [[int(v) for v in rng.integers(1, 16, size=u)] for u in tl]
+    b = W.make_batch(lengths, targets, 16, seed=B, sigma=1.0, reduction="mean")
+    compare(run_gpu(api, b), oracle_mod.ctc_batch(b), torch.float32, f"B={B}")
+
+
 def test_utterance_beyond_band_buckets(api, oracle_mod):
     # one utterance of 70000 frames: the streamed pipeline's band queue takes its exact-count order
     # (the bucketed order covers up to 65535 frames); a short one beside it

@@ -201,6 +201,29 @@ def test_many_short_utterances(api, oracle_mod, B):
     compare(run_gpu(api, b), oracle_mod.ctc_batch(b), torch.float32, f"B={B}")
 
 
+def test_concurrent_calls_on_two_streams(api, oracle_mod):
+    # two calls in flight at once, each on its own stream with its own workspace: on the streamed
+    # pipeline two persistent launches share the compute units, on the grouped one the library's
+    # group streams
+    _say("[gpu parity] two calls on two streams")
+    dev = torch.device("cuda:0")
+    batches = [W.make_workload("small"), W.make_workload("char_level")]
+    ins = [(b.log_probs.to(dev), b.cu_seqlens.to(dev), b.lengths.to(dev), b.targets.to(dev), b.target_lengths.to(dev))
+           for b in batches]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for b, x, st in zip(batches, ins, streams):
+        with torch.cuda.stream(st):
+            outs.append(api.packed_ctc_loss(*x, blank=b.blank, zero_infinity=b.zero_infinity, reduction=b.reduction,
+                                            max_target_length=int(b.target_lengths.max())))
+    torch.cuda.synchronize()
+    for b, (losses, reduced, grad) in zip(batches, outs):
+        got = {"loss": losses.cpu().double().numpy(), "reduced": float(reduced.cpu()),
+               "grad": grad.cpu().double().numpy()}
+        compare(got, oracle_mod.ctc_batch(b), torch.float32, f"{b.name} beside another call")
+
+
 def test_utterance_beyond_band_buckets(api, oracle_mod):
     # one utterance of 70000 frames: the streamed pipeline's band queue takes its exact-count order
     # (the bucketed order covers up to 65535 frames); a short one beside it

@@ -216,3 +216,63 @@ def test_pins_catch_planted_mistake(tmp_path, name):
         if caught:
             break
     assert caught, f"planted mistake {name} was not detected"
+
+
+def _mean_clamp_case():
+    # utterance 0 has no labels (U = 0: the mean divides its loss by max(U, 1) = 1), utterance 1 has
+    # two, utterance 2 one; values from the closed form of the empty target and from torch's CTC loss
+    return W.make_batch([6, 9, 4], [[], [1, 2], [3]], 5, seed=21, sigma=1.3, reduction="mean")
+
+
+def _check_mean_clamp(r, b):
+    """The loss module's mean (PR page, `ctc.py` `forward_packed`): each loss over its target length
+    clamped to at least 1, then the batch mean; the gradient weight of utterance b is 1 / (B max(U_b, 1)).
+    Expected values come from the U = 0 closed form (loss = -sum_t lp[t][blank], posterior all on the
+    blank) and from torch's float64 CTC loss, not from the oracle itself."""
+    import torch.nn.functional as F
+
+    lp = b.log_probs.double()
+    cu = b.cu_seqlens.numpy()
+    B = b.B
+    U = [int(u) for u in b.target_lengths]
+    losses = []
+    for i in range(B):
+        T = int(b.lengths[i])
+        rows = lp[cu[i]:cu[i] + T]
+        if U[i] == 0:
+            losses.append(float(-rows[:, b.blank].sum()))
+        else:
+            losses.append(float(F.ctc_loss(rows[:, None, :], b.targets[i:i + 1, :U[i]], [T], [U[i]], blank=b.blank,
+                                           reduction="none")[0]))
+    want = sum(l / max(u, 1) for l, u in zip(losses, U)) / B
+    np.testing.assert_allclose(r["reduced"], want, rtol=1e-12)
+    T0 = int(b.lengths[0])
+    rows0 = lp[cu[0]:cu[0] + T0].numpy()
+    onehot = np.zeros_like(rows0)
+    onehot[:, b.blank] = 1.0
+    np.testing.assert_allclose(r["grad"][cu[0]:cu[0] + T0], (np.exp(rows0) - onehot) / (B * 1), atol=1e-14)
+
+
+def test_mean_clamps_empty_target_length(oracle_mod):
+    b = _mean_clamp_case()
+    _check_mean_clamp(oracle_mod.ctc_batch(b), b)
+
+
+@pytest.mark.parametrize("site", ["weight", "reduced"])
+def test_mean_clamp_pin_catches_unclamped_divisor(tmp_path, site):
+    # planted mistake: the mean divides by U instead of max(U, 1) (in the gradient weight, or in the
+    # reduced loss); the pin above must reject the mutated oracle
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "ctc_oracle.c")).read()
+    old = {"weight": "w /= (double)B * (double)(U > 1 ? U : 1);",
+           "reduced": "total += l / (double)(U > 1 ? U : 1);"}[site]
+    assert old in src
+    mutated = tmp_path / "mut.c"
+    mutated.write_text(src.replace(old, old.replace("(U > 1 ? U : 1)", "U"), 1))
+    so = tmp_path / "libmut.so"
+    subprocess.check_call(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", str(mutated), "-o", str(so), "-lm"])
+    lib = oracle.load_library(str(so))
+    b = _mean_clamp_case()
+    r = oracle.ctc_packed(b.log_probs, b.cu_seqlens, b.lengths, b.targets, b.target_lengths, blank=b.blank,
+                          reduction="mean", lib=lib)
+    with pytest.raises(AssertionError):
+        _check_mean_clamp(r, b)

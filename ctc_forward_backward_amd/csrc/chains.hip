@@ -55,7 +55,6 @@ constexpr int kK = kChunk;             // frames per chunk (prefetch depth and r
 constexpr int kR = 128;                // LDS ring slots per wave boundary (4 chunks)
 constexpr int kWaves = kSegWaves;      // blocks per segment = waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kSpinLimit = 1 << 20;    // polls before a wave gives up waiting (about a second)
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer resource, gfx9 family
 constexpr int kStoreSc1 = 16;                 // cache policy of a buffer store: sc1, written through to device scope
 static_assert(2 * kK + 1 <= kEPad, "emission padding must cover two chunks of prefetch");
@@ -118,14 +117,22 @@ __device__ __forceinline__ bool lds_ok(unsigned long long v, int chunk) {
   return (slot_hi_of(v) & 0xffu) == (0x80u | (static_cast<uint32_t>(chunk) & 127u));
 }
 
+// Every wait on another wave is bounded in wall-clock time (wall_clock64(), a constant-rate counter;
+// the bound is a launch argument): a wave that runs out of time, or finds that another one already
+// has, raises the health word and carries on with whatever it holds, so every kernel ends.  Then
+// the losses of the call are NaN (weights kernel) and the gradient rows formed afterwards too.
+__device__ __forceinline__ bool out_of_time(uint64_t t0, int64_t ticks, int* err) {
+  return (int64_t)(wall_clock64() - t0) > ticks || gave_up(err);
+}
+
 // Bounded wait until every lane that `needs` it holds a written global slot (each lane re-reads
 // its own slot); on give-up the missing values are -inf at offset 0.  The waits are inline: a call
 // in the frame loop would make the compiler drain every load and store in flight at each chunk.
 __device__ __forceinline__ unsigned long long wait_global(const unsigned long long* p, unsigned long long v, bool need,
-                                                       int* err) {
-  int spins = 0;
+                                                       int64_t ticks, int* err) {
+  const uint64_t t0 = wall_clock64();
   while (__ballot(need && !global_ok(v))) {
-    if (++spins > kSpinLimit || gave_up(err)) {
+    if (out_of_time(t0, ticks, err)) {
       give_up(err);
       if (need && !global_ok(v)) v = pack(kNeg, 0x80u);
       break;
@@ -138,10 +145,10 @@ __device__ __forceinline__ unsigned long long wait_global(const unsigned long lo
 
 // the same for LDS slots tagged with the chunk each lane expects
 __device__ __forceinline__ unsigned long long wait_lds(const unsigned long long* p, unsigned long long v, bool need,
-                                                    int chunk, int* err) {
-  int spins = 0;
+                                                    int chunk, int64_t ticks, int* err) {
+  const uint64_t t0 = wall_clock64();
   while (__ballot(need && !lds_ok(v, chunk))) {
-    if (++spins > kSpinLimit || gave_up(err)) {
+    if (out_of_time(t0, ticks, err)) {
       give_up(err);
       if (need && !lds_ok(v, chunk)) v = pack(kNeg, 0x80u | (static_cast<uint32_t>(chunk) & 127u));
       break;
@@ -153,10 +160,10 @@ __device__ __forceinline__ unsigned long long wait_lds(const unsigned long long*
 }
 
 // bounded wait until the consumer wave has taken the neighbour values of chunk `c`
-__device__ __forceinline__ void wait_progress(int* prog, int c, int* err) {
-  int spins = 0;
+__device__ __forceinline__ void wait_progress(int* prog, int c, int64_t ticks, int* err) {
+  const uint64_t t0 = wall_clock64();
   while (__hip_atomic_load(prog, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < c) {
-    if (++spins > kSpinLimit || gave_up(err)) {
+    if (out_of_time(t0, ticks, err)) {
       give_up(err);
       return;
     }
@@ -185,41 +192,66 @@ struct Ctx {
   bool lout_live;
   int* prog_cons;
   int* prog_self;
-  int* sig;                 // this block's offset per chunk, at the row of the chunk's first frame
+  int* sig;                 // this block's per-lane offsets of the utterance's chunk 0 (64 ints per chunk)
   float* ab;                // this block's 128 states per row (row 0)
   bool store;               // keep the states and offsets (false: loss only, nothing is written)
   int* prog;                // streamed pipeline, the chain's last block: where it publishes its stored steps
   int* err;
+  int64_t ticks;            // wall-clock bound of every wait
   const Inputs* in;
   int64_t B;
 };
 
+// vmcnt(62) with the other counters left alone (gfx9 s_waitcnt encoding: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVm62 = (3 << 14) | (15 << 8) | (7 << 4) | 14;
+
 // The recursion of one block, specialised on the direction and on the kinds of its links, so that
 // the frame loop carries no branch on any of them.
+//
+// Offsets.  Every lane keeps an integer offset of its own, renormalised once per chunk to the floor of
+// its larger state, so a lane's values stay near 0 wherever its mass sits relative to the rest of the
+// block (with one offset per block, states carrying posterior mass can sit hundreds of units below
+// the block's largest, where float32 keeps few fraction bits, and the rounding of each step then
+// accumulates with the number of frames).  The neighbour value a lane takes each frame is moved into
+// its own offset by the integer difference of the two lanes' offsets, fixed over a chunk.
 //
 // STREAM (the streamed pipeline, where the posteriors of a frame are formed on other compute units,
 // possibly other XCDs, while the recursions still run): the states are stored write-through to the
 // device-coherent level (sc1) and the offsets with device-scope stores, and the chain's last block
 // (every other block of the chain is at least one chunk ahead of it) publishes how many steps are
-// stored.  At the start of chunk c it publishes the steps through chunk c-3: a wave has at most 63
-// vector-memory operations in flight and issues at least 64 per chunk (a label-emission load and a
-// state store per frame), so by then every store of chunk c-2 and before has completed.  The last
-// publication is a device-scope release after the last frame.
+// stored.  At the start of chunk c it waits until at most 62 of its vector memory operations are
+// outstanding (s_waitcnt vmcnt(62); the counter is decremented in issue order, loads and stores
+// alike, per the CDNA3 instruction set guide's data-dependency rules, which the compiler's own waits
+// in this loop rely on too) and, having issued at least 64 in chunk c-1 (a label-emission load and a
+// state store per frame), knows that every store of chunk c-2 and before has completed; then it
+// publishes the steps through chunk c-2.  A block ahead of it in the chain has issued its own chunk
+// c-1 and c operations since its chunk c-2 stores, so those have completed as well (at most 63
+// operations can be outstanding).  The last publication, after the last frame, is a device-scope
+// release.  The row side reads the progress word and then performs a device-scope acquire.
 template <bool BETA, bool IN_GLOBAL, bool OUT_GLOBAL, bool STREAM>
 __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
   const int lane = cx.lane, k = cx.k, T = cx.T, U = cx.U;
-  const int edge = BETA ? 0 : 63;
+  const int edge = BETA ? 0 : 63;      // the lane whose label this block passes on
+  const int edge_in = BETA ? 63 : 0;   // the lane that takes the producer's label
   const int64_t drow = BETA ? -1 : 1;
   const int64_t r0 = cx.start + (BETA ? T - 1 : 0);  // row of step 0
   const bool sk = cx.sk;
   const int64_t Es = cx.Es;
   int* err = cx.err;
+  const int64_t ticks = cx.ticks;
 
   auto dpp = [&](float old, float x) { return BETA ? dpp_f32<0x130>(old, x) : dpp_f32<0x138>(old, x); };
+  // the neighbour's label moved one lane and shifted into this lane's offset (the edge lane, which
+  // has no source lane, takes `old`, the producer's value, and a shift of 0)
+  auto dpp_shifted = [&](float old, float x, float sh) { return dpp(old, x) + sh; };
   auto row = [&](int64_t step) { return r0 + drow * step; };
   // lowest row of chunk c (its first frame for alpha, its last for beta) and a frame's place in it
   auto chunk_lo = [&](int c) { return BETA ? row((int64_t)(c + 1) * kK) : row(1 + (int64_t)c * kK); };
   auto in_chunk = [&](int i) { return BETA ? kK - 1 - i : i; };
+  // what the neighbour lane's value must gain to be in this lane's offset (0 on the edge lane, whose
+  // neighbour value comes through the ring, already converted)
+  auto lane_shift = [&](float off) { return dpp(off, off) - off; };
 
   // ---- first frame ----
   float xb, xl, off = 0.0f;
@@ -254,7 +286,7 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
     // build a lead over a producer in another segment: its slots are loaded a chunk ahead
     if (IN_GLOBAL && !cx.no_in) {
       const unsigned long long* p = cx.gin + row(min(2 * kK, T - 1));
-      wait_global(p, gload(p), true, err);
+      wait_global(p, gload(p), true, ticks, err);
     }
     // label emissions of chunk 0 (register i: the frame of step 1 + i); blank emissions and, across
     // a segment boundary, the neighbour slots of chunk 0, one per lane
@@ -284,23 +316,27 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
       const float ebn = P.Eb[row(1 + (int64_t)(c + 1) * kK + lk)];
       if (cx.store) {
         if (STREAM)
-          __hip_atomic_store(cx.sig + row(1 + (int64_t)c * kK), static_cast<int>(off), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(cx.sig + c * 64 + lane, static_cast<int>(off), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         else
-          cx.sig[row(1 + (int64_t)c * kK)] = static_cast<int>(off);
+          cx.sig[c * 64 + lane] = static_cast<int>(off);
       }
-      if (STREAM && cx.prog && c >= 3 && lane == 0)
-        __hip_atomic_store(cx.prog, (c - 2) * kK + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (STREAM && cx.prog && c >= 2) {
+        __builtin_amdgcn_s_waitcnt(kWaitVm62);
+        if (lane == 0) __hip_atomic_store(cx.prog, (c - 1) * kK + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       if (IN_GLOBAL) {
-        if (__ballot(need && !global_ok(raw))) raw = wait_global(cx.gin + row(min(c * kK + lk, nsteps)), raw, need, err);
+        if (__ballot(need && !global_ok(raw)))
+          raw = wait_global(cx.gin + row(min(c * kK + lk, nsteps)), raw, need, ticks, err);
         hraw = cx.no_in ? none : gload(cx.gin + row(min((c + 1) * kK + lk, nsteps)));
       } else {
-        if (__ballot(need && !lds_ok(raw, want))) raw = wait_lds(lp, raw, need, want, err);
+        if (__ballot(need && !lds_ok(raw, want))) raw = wait_lds(lp, raw, need, want, ticks, err);
         if (lane == 0) __hip_atomic_store(cx.prog_self, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
       // the consumer of this block's LDS ring must have taken the chunk whose slots this one reuses
-      if (check_cons && cons < c - (kR / kK - 1)) wait_progress(cx.prog_cons, c - (kR / kK - 1), err);
-      const float hv = slot_value(raw, off);
+      if (check_cons && cons < c - (kR / kK - 1)) wait_progress(cx.prog_cons, c - (kR / kK - 1), ticks, err);
+      // the producer's values in the offset of the lane that takes them
+      const float hv = slot_value(raw, lanef(off, edge_in));
+      const float shift = lane_shift(off);
       // loss only: a resource of no bytes, so the hardware discards the per-frame stores (range check)
       const __amdgpu_buffer_rsrc_t ab = __builtin_amdgcn_make_buffer_rsrc(cx.ab + chunk_lo(c) * 128, 0,
                                                                           cx.store ? kK * 512 : 0, kRsrcWord3);
@@ -311,7 +347,7 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
       unsigned long long* lslot = cx.lout + ((c * kK) & (kR - 1));
       // the neighbour of frame 0; each later frame's neighbour is formed as soon as the label value
       // it shifts exists, ahead of that frame's stores
-      float n = dpp(lanef(hv, 0), xl);
+      float n = dpp_shifted(lanef(hv, 0), xl, shift);
 #pragma unroll
       for (int i = 0; i < kK; ++i) {
         if (!FULL && i >= nvalid) continue;  // uniform: the last chunk's missing frames
@@ -328,7 +364,7 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
         // beta stores the sums before the emission: t for the blank, h2 + l2 for the label
         const float pl = BETA ? h2 + l2 : 0.0f;
         const float nl = BETA ? pl + el[i] : (h2 + el[i]) + l2;
-        if (i + 1 < kK) n = dpp(lanef(hv, i + 1), nl);
+        if (i + 1 < kK) n = dpp_shifted(lanef(hv, i + 1), nl, shift);
         el[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(er, cx.eidx * 4, in_chunk(i) * Es * 4, 0));
         xb = nb;
         xl = nl;
@@ -341,8 +377,9 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
           else lstore(lslot + i, v);
         }
       }
-      // shift by the block's integer maximum so the values stay near 0
-      const float mx = wave_max(fmaxf(xb, xl));
+      // each lane shifts by its own integer maximum so that its values stay near 0 (a lane without
+      // mass keeps its offset)
+      const float mx = fmaxf(xb, xl);
       const float d = mx > kNegHalf ? floorf(mx) : 0.0f;
       xb -= d;
       xl -= d;
@@ -363,18 +400,19 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
   const bool owner = BETA ? (cx.j == 0) : (cx.j == (U >> 6));
   if (!owner) return;
   float h = kNeg;
-  if (!BETA) {  // the producer's label at the last frame
+  if (!BETA) {  // the producer's label at the last frame, in the offset of lane 0 (the lane it feeds)
     const int step = T - 1;
+    const float off0 = lanef(off, 0);
     if (IN_GLOBAL) {
       const unsigned long long* p = cx.gin + row(step);
-      h = cx.no_in ? kNeg : slot_value(wait_global(p, gload(p), true, err), off);
+      h = cx.no_in ? kNeg : slot_value(wait_global(p, gload(p), true, ticks, err), off0);
     } else {
       const unsigned long long* p = cx.lin + ((step - 1) & (kR - 1));
-      h = slot_value(wait_lds(p, lload(p), true, chunk_of(step), err), off);
+      h = slot_value(wait_lds(p, lload(p), true, chunk_of(step), ticks, err), off0);
     }
   }
   // alpha: blank of pair U with the label of pair U-1; beta: blank of pair 0 with the label of pair 1
-  const float n = dpp(h, xl);
+  const float n = dpp(h, xl) + lane_shift(off);
   const float fin = lse2(xb, n);
   int rs = 0;
   for (int t = lane; t < T; t += 64) rs += P.rowoff[cx.start + t];
@@ -436,11 +474,12 @@ __device__ __forceinline__ void run_wave(const Inputs& in, const Layout& L, cons
   cx.lout = cx.lout_live ? sh.ring[beta ? w - 1 : w] : sh.ring[kWaves - 1];
   cx.prog_cons = &sh.prog[beta ? max(w - 1, 0) : min(w + 1, kWaves - 1)];
   cx.prog_self = &sh.prog[w];
-  cx.sig = P.sig + (dir * Gm + j) * TT;
+  cx.sig = P.sig + ((dir * Gm + j) * L.NCH + P.cbase[cx.b]) * 64;
   cx.ab = P.AB + (dir * Gm + j) * TT * 128;
   cx.store = store;
   cx.prog = (STREAM && (beta ? j == 0 : j == G - 1)) ? P.prog + chain : nullptr;
   cx.err = &P.ctl->err;
+  cx.ticks = in.wait_ticks;
   cx.in = &in;
   cx.B = L.B;
   // the recursions are the critical path: their waves win the SIMD over row kernels sharing it
@@ -490,10 +529,10 @@ __global__ void __launch_bounds__(kThreads, 1) chain_workers(Inputs in, Layout L
 // ---- streamed pipeline ----------------------------------------------------------------------------
 
 // bounded wait until a chain has published at least `steps` stored steps
-__device__ __forceinline__ void wait_steps(const int* prog, int steps, int* err) {
-  int spins = 0;
+__device__ __forceinline__ void wait_steps(const int* prog, int steps, int64_t ticks, int* err) {
+  const uint64_t t0 = wall_clock64();
   while (__hip_atomic_load(prog, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < steps) {
-    if (++spins > kSpinLimit || gave_up(err)) {
+    if (out_of_time(t0, ticks, err)) {
       give_up(err);
       return;
     }
@@ -502,10 +541,14 @@ __device__ __forceinline__ void wait_steps(const int* prog, int steps, int* err)
 }
 
 // Band k of utterance b (see kBand): one wave waits until both recursions have passed the band (the
-// others wait at the barrier, so polling stays one load per workgroup and microsecond), then its
-// rows are shared out over the workgroup's waves, one row per wave at a time.  Each row: the posteriors into the wave's LDS, then the gradient row; a row of an
-// utterance with a NaN input, no alignment or a zero weight is filled (NaN, or 0 where the weight
-// is 0 -- under zero_infinity an utterance without alignment has weight 0).
+// others wait at the barrier, so polling stays one load per workgroup and microsecond), then the
+// band's rows are shared out over the waves, one row per wave at a time.  The states and offsets the
+// recursions stored on other compute units are read with device-scope loads (rows.h: ld_dev), which
+// take the device-coherent copy; a device-scope acquire here instead (a cache invalidation per band)
+// measured 25-40 us slower per call.  Each row: the posteriors
+// into the wave's LDS, then the gradient row; a row of an utterance with a NaN input, no alignment
+// or a zero weight is filled (NaN, or 0 where the weight is 0 -- under zero_infinity an utterance
+// without alignment has weight 0), and after any give-up the rows are NaN.
 template <int DT>
 __device__ __forceinline__ void row_band(const Inputs& in, const Layout& L, const Pointers& P, void* grad,
                                          uint32_t* lds, int b, int k, int w, int lane, int& cur_b) {
@@ -516,21 +559,22 @@ __device__ __forceinline__ void row_band(const Inputs& in, const Layout& L, cons
   const int lo2 = T - 1 - re, hi2 = min(T - 1 - ra, ra - 1);        // and their mirrors
   const int n = n1 + max(hi2 - lo2 + 1, 0);
   if (w == 0) {
-    wait_steps(P.prog + 2 * b, re + 1, &P.ctl->err);
-    wait_steps(P.prog + 2 * b + 1, re + 1, &P.ctl->err);
+    wait_steps(P.prog + 2 * b, re + 1, in.wait_ticks, &P.ctl->err);
+    wait_steps(P.prog + 2 * b + 1, re + 1, in.wait_ticks, &P.ctl->err);
   }
   __syncthreads();  // (also keeps the compiler from moving the row's loads above the wait)
   if (w >= n) return;
+  const bool broken = __builtin_amdgcn_readfirstlane(gave_up(&P.ctl->err));
   const bool nan = m.flags & 1;
   const float w0 = utterance_weight(in, L.B, b, false);
   float* acc = reinterpret_cast<float*>(lds);
   for (int i = w; i < n; i += kStreamWaves) {
     const int t = i < n1 ? ra + i : lo2 + (i - n1);
     const int64_t r = (int64_t)m.start + t;
-    if (!nan && w0 != 0.0f && rows::posterior_stream(L, P, acc, r, b, w0, lane)) {
+    if (!broken && !nan && w0 != 0.0f && rows::posterior_stream(L, P, acc, r, b, w0, lane)) {
       rows::dense_row<DT, true>(in, L, P, grad, lds, r, b, w0, lane, cur_b);
     } else {
-      const bool zero = w0 == 0.0f || (!nan && in.zero_infinity);
+      const bool zero = !broken && (w0 == 0.0f || (!nan && in.zero_infinity));
       rows::fill_row<DT>(L, grad, r, zero ? 0.0f : __builtin_nanf(""), lane);
     }
   }
@@ -549,27 +593,34 @@ __global__ void __launch_bounds__(64 * kStreamWaves, 1) stream_workers(Inputs in
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint32_t* lds = reinterpret_cast<uint32_t*>(ssm + ((sizeof(Shared) + 15) & ~size_t(15))) + (int64_t)w * per_wave;
   GroupQ* q = &P.ctl->g[0];
-  const int qlen = q->qlen, nbands = P.ctl->nbands;
-  const int* items = P.items + q->itemoff;
-  int cur_b = -1;
+  const int qlen = q->qlen;
+  // Two phases, each its own loop, so that the band phase's values are not live (and do not take
+  // registers) while the recursion loop runs: first the recursion segments, then the bands; the
+  // first claim past the segments is the workgroup's first band.
+  int idx;
   for (;;) {
     for (int i = tid; i < kWaves * kR; i += 64 * kStreamWaves) (&sh.ring[0][0])[i] = 0ull;
     if (tid < kWaves) sh.prog[tid] = -1;
     if (tid == 0) sh.item = atomicAdd(&q->qcount, 1);
     __syncthreads();
-    const int idx = __builtin_amdgcn_readfirstlane(sh.item);
-    if (idx >= qlen + nbands) break;
-    if (idx < qlen) {
-      if (w < kWaves) {
-        const int item = __builtin_amdgcn_readfirstlane(items[idx]);
-        run_wave<true>(in, L, P, sh, item >> 12, item & 4095, w, lane, true);
-      }
-    } else {
-      const int2 bd = P.bands[idx - qlen];
-      row_band<DT>(in, L, P, grad, lds, __builtin_amdgcn_readfirstlane(bd.x), __builtin_amdgcn_readfirstlane(bd.y), w,
-                   lane, cur_b);
+    idx = __builtin_amdgcn_readfirstlane(sh.item);
+    if (idx >= qlen) break;
+    if (w < kWaves) {
+      const int item = __builtin_amdgcn_readfirstlane(P.items[q->itemoff + idx]);
+      run_wave<true>(in, L, P, sh, item >> 12, item & 4095, w, lane, true);
     }
     __syncthreads();
+  }
+  const int nbands = P.ctl->nbands;
+  int cur_b = -1;
+  while (idx < qlen + nbands) {
+    const int2 bd = P.bands[idx - qlen];
+    row_band<DT>(in, L, P, grad, lds, __builtin_amdgcn_readfirstlane(bd.x), __builtin_amdgcn_readfirstlane(bd.y), w,
+                 lane, cur_b);
+    __syncthreads();
+    if (tid == 0) sh.item = atomicAdd(&q->qcount, 1);
+    __syncthreads();
+    idx = __builtin_amdgcn_readfirstlane(sh.item);
   }
 }
 

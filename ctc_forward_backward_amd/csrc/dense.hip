@@ -41,10 +41,12 @@ __global__ void __launch_bounds__(256) dense_kernel(Inputs in, Layout L, Pointer
   int cur_b = -1;
   int64_t j0, j1;
   wave_share(P, group, wave_id(), (int64_t)gridDim.x * 4, j0, j1);
+  // a wave of the recursions gave up waiting: the rows are NaN (the losses too, weights kernel)
+  const bool broken = __builtin_amdgcn_readfirstlane(P.ctl->err) != 0;
   group_rows(P, group, j0, j1, [&](int64_t r, int b) {
     float w;
-    if (rows::row_live(P, b, w)) rows::dense_row<DT>(in, L, P, grad, lds, r, b, w, lane, cur_b);
-    else rows::fill_row<DT>(L, grad, r, w == 0.0f ? 0.0f : __builtin_nanf(""), lane);
+    if (!broken && rows::row_live(P, b, w)) rows::dense_row<DT>(in, L, P, grad, lds, r, b, w, lane, cur_b);
+    else rows::fill_row<DT>(L, grad, r, !broken && w == 0.0f ? 0.0f : __builtin_nanf(""), lane);
   });
 }
 

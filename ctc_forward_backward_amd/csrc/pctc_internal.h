@@ -36,7 +36,7 @@ struct Meta {
 
 // Workspace carve-up.  Every region is 256-byte aligned.
 // Frames per chunk of the recursions: their prefetch depth and the period of their integer shift.
-// A block's offset is stored once per chunk, at the row of the chunk's first frame.
+// Each lane (state pair) keeps an integer offset of its own, stored once per chunk.
 constexpr int kChunk = 32;
 
 // 64-pair state blocks per segment of a recursion: the waves of one workgroup, one per SIMD, linked
@@ -58,7 +58,8 @@ struct Layout {
   int64_t Gmax;      // state-pair blocks of the longest target: ceil((Umax + 1) / 64)
   int64_t Dw;        // 32-bit words of a class bitmap: ceil(D / 32)
   int64_t C_stride;  // floats per row of the compact class sums (>= Umax + 1)
-  size_t off_cbits, off_cpref, off_dmap, off_meta, off_lab, off_rowmap, off_rowoff, off_E, off_Eb, off_AB, off_nll, off_llb, off_lsh, off_w, off_post, off_order, off_cum, off_ring,
+  int64_t NCH;       // chunk slots of the per-lane offsets: >= sum over utterances of ceil((T - 1) / kChunk)
+  size_t off_cbase, off_cbits, off_cpref, off_dmap, off_meta, off_lab, off_rowmap, off_rowoff, off_E, off_Eb, off_AB, off_nll, off_llb, off_lsh, off_w, off_post, off_order, off_cum, off_ring,
       off_sig, off_items, off_ctl, off_prog, off_bands, total;
 };
 
@@ -83,7 +84,7 @@ struct GroupQ {
 
 // control words of the recursion work queues
 struct ChainCtl {
-  int err;      // non-zero: a block gave up waiting for its neighbour (results unspecified)
+  int err;      // non-zero: a wave gave up a bounded wait; the losses of the call are NaN
   int ngroups;
   int nbands;   // streamed pipeline: row bands queued after group 0's recursion segments
   int pad[5];
@@ -109,14 +110,18 @@ struct Pointers {
   float* Eb;     // (T_total,): column 0 of E (the blank) again, contiguous for the recursions; kEPad padding each side
   // (2, Gmax, T_total, 128): normalised log2 alpha (direction 0) and beta (direction 1) per block
   // of 64 state pairs and per row.  Alpha pair k sits at 2k, 2k+1 (states 2k, 2k+1); beta pair k at
-  // 2k, 2k+1 (states 2k-1, 2k), i.e. beta of state s at position s+1, all relative to the block.
+  // 2k, 2k+1 (states 2k-1, 2k), i.e. beta of state s at position s+1, each relative to its lane's
+  // offset for that chunk (sig).
   float* AB;
   double* nll;   // (B,) raw negative log-likelihood in nats (+inf: no alignment)
   double* llb;   // (B,) log2 likelihood from the beta side (consistency check)
   double* lsh;   // (B,) log2 likelihood from the alpha side without the row offsets
   float* w;      // (B,) gradient weight
   unsigned long long* ring;  // (2, Gmax, T_total) block-boundary values (value, offset) per frame
-  int* sig;      // (2, Gmax, T_total) integer offset of each block's stored values, per chunk
+  // (2, Gmax, NCH, 64) integer offset of each lane's stored values (its state pair), per chunk: chunk c
+  // of utterance b at slot cbase[b] + c
+  int* sig;
+  int* cbase;    // (B + 1) first chunk slot of each utterance (exclusive prefix of ceil((T - 1) / kChunk))
   int* items;    // (2 B Gmax) queued recursion segments, by group: (utterance * 2 + direction) << 12 | segment
   int* order;    // (B) utterances by frame count, longest first (ties by index)
   int* cum;      // (B) per sorted position: rows of the group's earlier utterances
@@ -400,6 +405,7 @@ struct Inputs {
   int zero_infinity;
   int reduction;
   const float* grad_scale;
+  int64_t wait_ticks;  // bound of every wait on another wave, in wall_clock64() ticks
 };
 
 // The gradient weight of utterance b: grad_scale[b] (or 1), over B * max(U, 1) for the mean (U as

@@ -221,8 +221,11 @@ __global__ void __launch_bounds__(256) weights_kernel(Inputs in, Layout L, Point
   __shared__ double part[256];
   double acc = 0.0;
   const int64_t B = L.B;
+  // a wave of the recursions gave up a bounded wait: the results of the call are unspecified, and
+  // every loss and the reduced value say so with NaN
+  const bool broken = P.ctl->err != 0;
   for (int64_t b = threadIdx.x; b < B; b += blockDim.x) {
-    const double nll = P.nll[b];
+    const double nll = broken ? (double)NAN : P.nll[b];
     const bool inf = nll == (double)INFINITY;
     const double loss = (in.zero_infinity && inf) ? 0.0 : nll;
     if (losses_out) losses_out[b] = static_cast<float>(loss);
@@ -244,7 +247,7 @@ __global__ void __launch_bounds__(256) weights_kernel(Inputs in, Layout L, Point
   if (threadIdx.x == 0 && reduced_out && in.reduction != 0) {
     double v = part[0];
     if (in.reduction == 2) v = B > 0 ? v / (double)B : (double)NAN;
-    *reduced_out = static_cast<float>(v);
+    *reduced_out = static_cast<float>(broken ? (double)NAN : v);
   }
 }
 
@@ -325,6 +328,14 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
   // half the rows on the caller's stream, then the middle, then the short ones, whose gathers,
   // recursions and rows all finish under the long recursions
   const float share[kMaxGroups][kMaxGroups] = {{1.0f, 1.0f, 1.0f}, {0.15f, 1.0f, 1.0f}, {0.45f, 0.75f, 1.0f}};
+  // first slot of each utterance's chunks in the per-lane offset table: chunk c holds steps
+  // 1 + c kChunk .. (c + 1) kChunk, so an utterance of T frames has ceil((T - 1) / kChunk) chunks
+  for (int b = tid; b < B; b += nt) {
+    const int T = P.meta[b].T;
+    P.cbase[b] = T > 1 ? (T - 1 + kChunk - 1) / kChunk : 0;
+  }
+  __syncthreads();
+  block_exclusive_scan(P.cbase, B, wsum);
   if (sort) {
     int* sT = sh;
     int* order = sh + B;

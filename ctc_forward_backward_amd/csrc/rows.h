@@ -12,7 +12,7 @@
 // Design for gfx950:
 //   - posterior_row: one pass over the stored alpha and beta (beta is stored without the frame's
 //     own emission, so alpha + beta is already alpha + beta - lp), 2^(alpha + beta) taken relative
-//     to the likelihood the alpha recursion reached (the block offsets of alpha and beta meet in
+//     to the likelihood the alpha recursion reached (the per-lane offsets of alpha and beta meet in
 //     that constant, so every term is at most about 1).  Blank states are summed in registers,
 //     label states added into an LDS array indexed by the rank of their class among the
 //     utterance's classes (at most U+1 entries).  The frame's own total z of the terms normalises
@@ -55,12 +55,14 @@ __device__ __forceinline__ void posterior_row(const Layout& L, const Pointers& P
   const Meta m = P.meta[b];
   const int U = m.U, G = (U + 64) >> 6;
   const int64_t start = m.start, T = m.T;
-  // each recursion block stores its offset once per chunk, at the row of the chunk's first frame
+  // every lane of a recursion block stores its offset once per chunk; the first frame (step 0) has
+  // offset 0
   const int64_t sa = r - start, sb = start + T - 1 - r;
-  const int64_t rowa = sa == 0 ? -1 : start + 1 + ((sa - 1) / kChunk) * kChunk;
-  const int64_t rowb = sb == 0 ? -1 : start + T - 1 - (1 + ((sb - 1) / kChunk) * kChunk);
-  auto offA = [&](int j) { return rowa < 0 ? 0 : P.sig[j * TT + rowa]; };
-  auto offB = [&](int j) { return rowb < 0 ? 0 : P.sig[(Gm + j) * TT + rowb]; };
+  const int64_t NC = L.NCH, cb0 = P.cbase[b];
+  const int64_t slotA = sa == 0 ? -1 : cb0 + (sa - 1) / kChunk;
+  const int64_t slotB = sb == 0 ? -1 : cb0 + (sb - 1) / kChunk;
+  auto offA = [&](int j, int ln) { return slotA < 0 ? 0 : P.sig[((int64_t)j * NC + slotA) * 64 + ln]; };
+  auto offB = [&](int j, int ln) { return slotB < 0 ? 0 : P.sig[((Gm + j) * NC + slotB) * 64 + ln]; };
   const double lsh = P.lsh[b];
   const int* dmap = P.dmap + (int64_t)b * (L.Umax + 1);
   // LDS operations of one wave complete in order: zeroing, atomics and reads need no barrier
@@ -81,8 +83,9 @@ __device__ __forceinline__ void posterior_row(const Layout& L, const Pointers& P
       c0[u] = c1[u] = 0.0f;
       d1[u] = 0;
       if (j < G) {
-        const int oa = offA(j), ob0 = offB(j);
-        const int ob1 = lane < 63 ? ob0 : (j + 1 < G ? offB(j + 1) : ob0);
+        // state 2k: alpha and beta of this lane; state 2k+1: alpha of this lane, beta of the next
+        const int oa = offA(j, lane), ob0 = offB(j, lane);
+        const int ob1 = lane < 63 ? offB(j, lane + 1) : (j + 1 < G ? offB(j + 1, 0) : ob0);
         c0[u] = static_cast<float>((double)(oa + ob0) - lsh);
         c1[u] = static_cast<float>((double)(oa + ob1) - lsh);
         const int64_t rb = ((Gm + j) * TT + r) * 128;
@@ -115,12 +118,27 @@ __device__ __forceinline__ void posterior_row(const Layout& L, const Pointers& P
   for (int i = lane; i <= U; i += 64) out[i] = acc[i] * scale;
 }
 
+// device-scope loads (sc1): they read the device-coherent copy, never a line an earlier access left
+// in a cache, so data that recursions on other compute units stored and then published is seen
+// without a cache invalidation on the reading side
+__device__ __forceinline__ int ld_dev(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __builtin_bit_cast(float, __hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ float2 ld_dev2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__builtin_bit_cast(float, static_cast<uint32_t>(v)), __builtin_bit_cast(float, static_cast<uint32_t>(v >> 32)));
+}
+
 // Streamed pipeline: the posteriors of row r of utterance b while the recursions may still be running
 // (the band scheduler has seen both pass this frame).  The likelihood is not known yet, so the
 // exponent reference is an integer found on the way: the first batch of blocks with mass sets it at
 // its largest term, a later batch with a larger term raises it and scales the sums so far down.  The
-// block offsets are read with device-coherent loads: a chunk's offset shares its cache line with
-// offsets of later chunks, which may be stored after this line was cached.  Leaves the row's class
+// states and the per-lane offsets are read with device-scope loads (ld_dev).  Leaves the row's class
 // sums times w / z in acc (U+1 floats, by class rank); false when the frame carries no mass (the
 // utterance has no alignment).
 __device__ __forceinline__ bool posterior_stream(const Layout& L, const Pointers& P, float* acc, int64_t r, int b,
@@ -130,15 +148,16 @@ __device__ __forceinline__ bool posterior_stream(const Layout& L, const Pointers
   const int U = m.U, G = (U + 64) >> 6;
   const int64_t start = m.start, T = m.T;
   const int64_t sa = r - start, sb = start + T - 1 - r;
-  const int64_t rowa = sa == 0 ? -1 : start + 1 + ((sa - 1) / kChunk) * kChunk;
-  const int64_t rowb = sb == 0 ? -1 : start + T - 1 - (1 + ((sb - 1) / kChunk) * kChunk);
-  auto sig = [&](int64_t i) { return __hip_atomic_load(P.sig + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
-  auto offA = [&](int j) { return rowa < 0 ? 0 : sig(j * TT + rowa); };
-  auto offB = [&](int j) { return rowb < 0 ? 0 : sig((Gm + j) * TT + rowb); };
+  const int64_t NC = L.NCH, cb0 = P.cbase[b];
+  const int64_t slotA = sa == 0 ? -1 : cb0 + (sa - 1) / kChunk;
+  const int64_t slotB = sb == 0 ? -1 : cb0 + (sb - 1) / kChunk;
+  auto offA = [&](int j, int ln) { return slotA < 0 ? 0 : ld_dev(P.sig + ((int64_t)j * NC + slotA) * 64 + ln); };
+  auto offB = [&](int j, int ln) { return slotB < 0 ? 0 : ld_dev(P.sig + ((Gm + j) * NC + slotB) * 64 + ln); };
   const int* dmap = P.dmap + (int64_t)b * (L.Umax + 1);
   for (int i = lane; i <= U; i += 64) acc[i] = 0.0f;
 
-  int ref = offA(0) + offB(0);
+  // the reference starts at 0 and moves to the first batch with mass (no round trip of its own)
+  int ref = 0;
   bool have = false;
   float z = 0.0f, bsum = 0.0f;
   for (int j0 = 0; j0 < G; j0 += kBlocks) {
@@ -155,16 +174,17 @@ __device__ __forceinline__ bool posterior_stream(const Layout& L, const Pointers
       c0[u] = c1[u] = 0;
       d1[u] = 0;
       if (j < G) {
-        const int oa = offA(j), ob0 = offB(j);
-        const int ob1 = lane < 63 ? ob0 : (j + 1 < G ? offB(j + 1) : ob0);
+        // state 2k+1 takes beta (and its offset) from the next lane: lane 63 from the next block's lane 0
+        const int jn = lane < 63 ? j : min(j + 1, G - 1), ln = lane < 63 ? lane + 1 : 0;
+        const int oa = offA(j, lane), ob0 = offB(j, lane), ob1 = offB(jn, ln);
         const int64_t rb = ((Gm + j) * TT + r) * 128;
         c0[u] = oa + ob0 - ref;
         c1[u] = oa + ob1 - ref;
         if (k <= U) {
-          const float2 a = *reinterpret_cast<const float2*>(P.AB + ((int64_t)j * TT + r) * 128 + 2 * lane);
-          s0[u] = a.x + P.AB[rb + 2 * lane + 1];
+          const float2 a = ld_dev2(P.AB + ((int64_t)j * TT + r) * 128 + 2 * lane);
+          s0[u] = a.x + ld_dev(P.AB + rb + 2 * lane + 1);
           if (k < U) {
-            s1[u] = a.y + P.AB[lane < 63 ? rb + 2 * lane + 2 : rb + TT * 128];
+            s1[u] = a.y + ld_dev(P.AB + (lane < 63 ? rb + 2 * lane + 2 : rb + TT * 128));
             d1[u] = dmap[k + 1];
           }
         }

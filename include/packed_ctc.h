@@ -174,12 +174,24 @@ int packed_ctc_reduce(const float* losses, const void* target_lengths, int index
                       float* out, void* stream);
 
 /*
- * Health word of the last packed_ctc_loss call that used this workspace.  The recursions of one
- * utterance run as a pipeline of blocks that wait on each other with a bounded spin; a block that
- * gives up sets a flag and the results of that call are unspecified.  Waits for `stream`, then
- * stores 0 (healthy) or non-zero in *status_out.
+ * Health word of the last call that used this workspace.  The recursions of one utterance run as a
+ * pipeline of state blocks that wait on each other, and the rows of the streamed pipeline wait on
+ * the recursions; every such wait is bounded in wall-clock time (packed_ctc_set_wait_limit).  A wave
+ * that runs out of time sets the health word and carries on, so every kernel still ends; the call
+ * then writes NaN into every entry of losses_out and into reduced_out, and its gradient is
+ * unspecified (the rows formed after the give-up are NaN).  Waits for `stream`, then stores 0
+ * (healthy) or non-zero in *status_out.
  */
 int packed_ctc_workspace_status(const void* workspace, void* stream, int* status_out);
+
+/*
+ * Wall-clock bound, in microseconds, of each wait of one wave on another inside the kernels
+ * (default 2 s, far beyond any wait of a healthy call; 0 makes every wait that is not met at once
+ * give up, which tests use to check the failure path).  Process-wide; read when a call is enqueued.
+ * Returns PCTC_OK, or PCTC_ERR_ARG outside [0, 3600 s].  packed_ctc_wait_limit returns the bound.
+ */
+int packed_ctc_set_wait_limit(int64_t microseconds);
+int64_t packed_ctc_wait_limit(void);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* packed_ctc_last_error(void);

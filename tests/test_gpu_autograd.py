@@ -3,17 +3,20 @@ capture, on the GPU, through the C ABI.
 
 - The split call gives the fused call's losses and gradient (the same kernels; float32 workloads,
   within 1e-6, since class sums are accumulated with LDS atomics in no fixed order).
-- The backward with upstream weights matches the float64 oracle with those weights as grad_scale,
-  at the parity tolerances (losses 1e-4 / 2e-3 relative, gradients 1e-4 / 2e-3 absolute for
-  float32 / 16-bit inputs; for the gradient, beyond half an ulp of the stored dtype at the exact
-  value, and times max(1, |w_b|) on the rows of utterance b: the bar is set for unit weights, and
-  an upstream weight scales the gradient and its error, while the stored value's own rounding
-  grows with its magnitude);
-  a second backward on the same forward state matches as well.
+- The backward with upstream weights in [-1, 1] matches the float64 oracle with those weights as
+  grad_scale, at the parity tolerances (losses 1e-4 / 2e-3 relative, gradients 1e-4 / 2e-3
+  absolute for float32 / 16-bit inputs); a second backward on the same forward state matches as
+  well.
 - Autograd (`ctc_loss` + `.backward`) for none / sum / mean matches the oracle.
 - A captured graph of the fused call and one of the autograd forward + backward, with the target
   bound set to the targets width (no host read), replayed several times on fresh inputs with eager
   work between replays: every replay matches an eager call on the same inputs.
+- The page's graph-replay scenario (PR page, test file, `test_cuda_graph_replay`), with seeded
+  values of our own: a capture sized by the targets width, then replays after new targets, target
+  lengths and frame lengths are copied into the captured buffers (a target as long as the width,
+  empty targets, a zero-length utterance, junk past every length); each replay is compared with
+  the float64 oracle on that replay's metadata, on both pipelines of the fused call and through
+  autograd.
 """
 
 import numpy as np
@@ -46,26 +49,10 @@ def _dev_args(b):
     return (b.cu_seqlens.to(dev), b.lengths.to(dev), b.targets.to(dev), b.target_lengths.to(dev))
 
 
-def _row_scale(b, gs):
-    """Per-row tolerance factor max(1, |w_b|): the bar is for unit weights, and an upstream weight w
-    scales the gradient, and the rounding of its stored 16-bit value, by |w|."""
-    f = np.ones(int(b.T_total))
-    cu, ln = b.cu_seqlens.numpy(), b.lengths.numpy()
-    for i in range(int(b.B)):
-        f[int(cu[i]):int(cu[i]) + int(ln[i])] = max(1.0, abs(float(gs[i])))
-    return f
-
-
-def _half_ulp(x, dtype):
-    """Half a unit in the last place of `dtype` at |x| (the most that rounding the exact value to the
-    stored dtype moves it): 2^(e-8) for bfloat16, 2^(e-11) for float16 with |x| in [2^e, 2^(e+1))."""
-    bits = {torch.bfloat16: 8, torch.float16: 11, torch.float32: 24}[dtype]
-    ax = np.abs(x)
-    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
-    return np.where(ax > 0, np.exp2(e - bits), 0.0)
-
-
-def _check_oracle(losses, grad, ref, dtype, label, row_scale=None):
+def _check_oracle(losses, grad, ref, dtype, label):
+    """The parity bar: losses within 1e-4 / 2e-3 relative, gradients within 1e-4 / 2e-3 absolute
+    (float32 / 16-bit inputs).  The upstream weights of these tests lie in [-1, 1], so every
+    gradient entry stays within the unit-weight range the bar is set for."""
     lrt, gat = TOL[dtype]
     loss = losses.detach().cpu().double().numpy()
     rloss = ref["loss"]
@@ -77,12 +64,9 @@ def _check_oracle(losses, grad, ref, dtype, label, row_scale=None):
         rg = ref["grad"]
         nan_ref = np.isnan(rg)
         assert np.array_equal(np.isnan(g), nan_ref), label
-        scale = np.ones(g.shape[0]) if row_scale is None else row_scale
-        rgf = np.nan_to_num(rg)
-        # the bar scaled by max(1, |w_b|), beyond the rounding of the exact value to the stored dtype
-        err = (np.maximum(np.abs(np.nan_to_num(g) - rgf) - _half_ulp(rgf, dtype), 0.0) / scale[:, None])[~nan_ref]
+        err = np.abs(g - rg)[~nan_ref]
         worst = float(err.max()) if err.size else 0.0
-        _say(f"  {label}: max (|grad err| - half ulp) / max(1, |w|) = {worst:.3e} (tol {gat})")
+        _say(f"  {label}: max |grad err| = {worst:.3e} (tol {gat})")
         assert worst <= gat, f"{label}: gradient error {worst} > {gat}"
 
 
@@ -112,12 +96,12 @@ def test_backward_weights_vs_oracle(api, oracle_mod, name):
                                               reduction="none")
     rng = np.random.default_rng(21)
     for k in range(2):  # the same forward state serves two backward calls
-        gs = rng.normal(0.0, 1.0, size=b.B).astype(np.float32)
+        gs = rng.uniform(-1.0, 1.0, size=b.B).astype(np.float32)
         gs[0] = 0.0
         grad = api.packed_ctc_backward(state, torch.from_numpy(gs), zero_infinity=b.zero_infinity, reduction="none")
         torch.cuda.synchronize()
         ref = oracle_mod.ctc_batch(b, reduction="none", grad_scale=gs.astype(np.float64))
-        _check_oracle(losses, grad, ref, b.log_probs.dtype, f"{name}/backward {k}", _row_scale(b, gs))
+        _check_oracle(losses, grad, ref, b.log_probs.dtype, f"{name}/backward {k}")
     assert api.last_call_status() == 0
 
 
@@ -128,7 +112,7 @@ def test_autograd_vs_oracle(api, oracle_mod, reduction):
     lp = b.log_probs.to("cuda:0").requires_grad_(True)
     out = api.ctc_loss(lp, *_dev_args(b), blank=b.blank, zero_infinity=b.zero_infinity, reduction=reduction)
     if reduction == "none":
-        g = torch.linspace(-1.5, 2.0, b.B, dtype=torch.float32, device="cuda:0")
+        g = torch.linspace(-1.0, 1.0, b.B, dtype=torch.float32, device="cuda:0")
         out.backward(g)
         gs = g.cpu().double().numpy()
     else:
@@ -138,7 +122,7 @@ def test_autograd_vs_oracle(api, oracle_mod, reduction):
     torch.cuda.synchronize()
     ref = oracle_mod.ctc_batch(b, reduction=reduction, grad_scale=gs)
     losses = out if reduction == "none" else torch.from_numpy(ref["loss"])  # scalar checked below
-    _check_oracle(losses, lp.grad, ref, b.log_probs.dtype, f"autograd/{reduction}", _row_scale(b, gs))
+    _check_oracle(losses, lp.grad, ref, b.log_probs.dtype, f"autograd/{reduction}")
     if reduction != "none":
         np.testing.assert_allclose(float(out.detach().cpu()), ref["reduced"], rtol=1e-4)
     assert lp.grad.dtype == lp.dtype
@@ -255,3 +239,92 @@ def test_graph_capture_as_first_call(api):
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     r = subprocess.run([sys.executable, "-c", _FIRST_CALL_CAPTURED, root], capture_output=True, text=True, timeout=110)
     assert r.returncode == 0 and "OK" in r.stdout, (r.stdout[-2000:], r.stderr[-2000:])
+
+
+def _replay_batches():
+    """Metadata of the page's graph-replay scenario: four utterances in fixed row slots
+    (cu_seqlens [0, 70, 77, 81, 81], D = 6, blank 5), a (4, 32) targets buffer; per replay new labels
+    (junk past each length), target lengths and frame lengths."""
+    rng = np.random.default_rng(19)
+    out = []
+    for tl, ln in (([4, 3, 2, 0], [70, 7, 4, 0]), ([32, 2, 1, 0], [70, 7, 4, 0]), ([0, 1, 2, 0], [66, 7, 0, 0]),
+                   ([32, 3, 0, 0], [70, 5, 4, 0])):
+        tg = rng.integers(0, 5, size=(4, 32))
+        out.append((torch.tensor(tg, dtype=torch.int64), torch.tensor(tl, dtype=torch.int64),
+                    torch.tensor(ln, dtype=torch.int64)))
+    return out
+
+
+def _replay_case():
+    b = W.make_batch([70, 7, 4, 0], [[1, 2, 3, 4], [0, 1, 2], [3, 3], []], 6, seed=19, sigma=1.0, blank=5,
+                     width=32)
+    return b
+
+
+def _oracle_for(oracle_mod, lp, cu, tg, tl, ln):
+    return oracle_mod.ctc_packed(lp, cu, ln, tg, tl, blank=5, reduction="none")
+
+
+@pytest.mark.parametrize("pipeline", ["streamed", "grouped"])
+def test_graph_replay_new_metadata_fused(api, oracle_mod, pipeline):
+    _say(f"[gpu autograd] graph replay with new targets / lengths, fused call, pipeline {pipeline}")
+    api.set_pipeline(pipeline)
+    try:
+        b = _replay_case()
+        dev = torch.device("cuda:0")
+        lp = b.log_probs.to(dev)
+        cu = b.cu_seqlens.to(dev)
+        ln = b.lengths.to(dev)
+        tg = b.targets.to(dev)
+        tl = b.target_lengths.to(dev)
+        kw = dict(blank=5, reduction="none", max_target_length=32)
+        api.packed_ctc_loss(lp, cu, ln, tg, tl, **kw)  # eager first (the library's group streams)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            losses, _, grad = api.packed_ctc_loss(lp, cu, ln, tg, tl, **kw)
+        for k, (ntg, ntl, nln) in enumerate(_replay_batches()):
+            tg.copy_(ntg.to(dev))
+            tl.copy_(ntl.to(dev))
+            ln.copy_(nln.to(dev))
+            graph.replay()
+            torch.cuda.synchronize()
+            assert api.last_call_status() == 0
+            ref = _oracle_for(oracle_mod, b.log_probs, b.cu_seqlens, ntg, ntl, nln)
+            _check_oracle(losses, grad, ref, torch.float32, f"replay {k} U={ntl.tolist()} T={nln.tolist()}")
+            api.packed_ctc_loss(lp, cu, ln, tg, tl, **kw)  # eager work between replays
+            torch.cuda.synchronize()
+            assert float(losses[3]) == 0.0
+    finally:
+        api.set_pipeline("streamed")
+
+
+def test_graph_replay_new_metadata_autograd(api, oracle_mod):
+    _say("[gpu autograd] graph replay with new targets / lengths, autograd forward + backward")
+    b = _replay_case()
+    dev = torch.device("cuda:0")
+    lp = b.log_probs.to(dev).clone().requires_grad_(True)
+    cu = b.cu_seqlens.to(dev)
+    ln = b.lengths.to(dev)
+    tg = b.targets.to(dev)
+    tl = b.target_lengths.to(dev)
+    kw = dict(blank=5, reduction="none", max_target_length=32)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        api.ctc_loss(lp, cu, ln, tg, tl, **kw).sum().backward()
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    lp.grad = None
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = api.ctc_loss(lp, cu, ln, tg, tl, **kw)
+        out.sum().backward()
+    for k, (ntg, ntl, nln) in enumerate(_replay_batches()):
+        tg.copy_(ntg.to(dev))
+        tl.copy_(ntl.to(dev))
+        ln.copy_(nln.to(dev))
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = _oracle_for(oracle_mod, b.log_probs, b.cu_seqlens, ntg, ntl, nln)
+        _check_oracle(out, lp.grad, ref, torch.float32, f"autograd replay {k} U={ntl.tolist()} T={nln.tolist()}")

@@ -244,13 +244,11 @@ def test_utterance_beyond_band_buckets(api, oracle_mod):
     # the two pipelines share the recursions: their posteriors agree to float32 rounding
     assert float(np.max(np.abs(got["grad"] - other["grad"]))) <= 1e-5
     np.testing.assert_allclose(got["loss"], ref["loss"], rtol=1e-4)
-    # against the float64 oracle the bound is looser than the workloads' 1e-4: rounding in the
-    # float32 log-space recursion accumulates over the steps (the loss, 1.7e5 nats here, carries
-    # about 0.02 nats of it), and at 70000 frames the posteriors differ from the exact ones by up to
-    # 8e-4 on either pipeline (at the workloads' 3000 frames, by 2.4e-7)
+    # the recursions keep an integer offset per state pair, so float32 rounding does not accumulate
+    # with the number of frames (with one offset per 64-pair block this case drifted to 8e-4)
     err = float(np.max(np.abs(got["grad"] - ref["grad"])))
-    _say(f"  T=70000: max |grad err| = {err:.3e} (long-utterance bound 2e-3)")
-    assert err <= 2e-3
+    _say(f"  T=70000: max |grad err| = {err:.3e} (bar 1e-4)")
+    assert err <= 1e-4
 
 
 def test_large_vocabulary_lds_accumulator(api, oracle_mod):
@@ -279,7 +277,7 @@ def test_host_read_errors(api):
     args = (b.log_probs.to(dev), b.cu_seqlens.to(dev), b.lengths.to(dev), b.targets.to(dev))
     with pytest.raises(ValueError, match="negative"):
         api.packed_ctc_loss(*args, torch.tensor([3, -1, 2, 2], device=dev), blank=0)
-    with pytest.raises(ValueError, match="targets width"):
+    with pytest.raises(ValueError, match="targets row"):
         api.packed_ctc_loss(*args, b.target_lengths.to(dev) + 100, blank=0)
     with pytest.raises(TypeError, match="float32"):  # float64 is accepted (its own path); integers are not
         api.packed_ctc_loss(b.log_probs.to(torch.int32).to(dev), *args[1:], b.target_lengths.to(dev), blank=0)
@@ -346,3 +344,31 @@ def test_maximum_sizes(api, oracle_mod):
     b = W.make_batch([90, 41, 5], targets, lim_d, seed=13, sigma=3.0, dtype="bf16", blank=lim_d - 1,
                      reduction="mean")
     compare(run_gpu(api, b), oracle_mod.ctc_batch(b), torch.bfloat16, f"D={lim_d}")
+
+
+def test_wait_give_up_poisons_the_call(api, oracle_mod):
+    """Every wait of one wave on another is bounded in wall-clock time.  With the bound set to 0 from
+    the host, the waits that are not met at once give up; every kernel still ends, the call's losses
+    and reduced value come back NaN and the workspace status is non-zero.  A call after the bound is
+    restored is healthy and matches the oracle."""
+    _say("[gpu parity] bounded waits forced to give up (wait limit 0)")
+    rng = np.random.default_rng(23)
+    lengths = [1800, 900, 300]
+    tl = [600, 250, 40]  # 10, 4 and 1 state blocks: a chain of three segments, one of one segment
+    targets = [[int(x) for x in rng.integers(1, 40, size=u)] for u in tl]
+    b = W.make_batch(lengths, targets, 40, seed=23, sigma=1.5, reduction="sum")
+    dev = torch.device("cuda:0")
+    old = api.wait_limit()
+    api.set_wait_limit(0)
+    try:
+        losses, reduced, grad = api.packed_ctc_loss(b.log_probs.to(dev), b.cu_seqlens.to(dev), b.lengths.to(dev),
+                                                    b.targets.to(dev), b.target_lengths.to(dev), blank=b.blank,
+                                                    reduction="sum", max_target_length=max(tl))
+        torch.cuda.synchronize()
+        status = api.last_call_status()
+    finally:
+        api.set_wait_limit(old)
+    _say(f"  status {status}, losses {losses.cpu().tolist()}")
+    assert status != 0
+    assert bool(torch.isnan(losses).all()) and bool(torch.isnan(reduced))
+    compare(run_gpu(api, b), oracle_mod.ctc_batch(b), torch.float32, "after the bound is restored")

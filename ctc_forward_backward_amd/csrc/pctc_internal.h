@@ -404,16 +404,31 @@ struct Inputs {
   int blank;
   int zero_infinity;
   int reduction;
-  const float* grad_scale;
+  const void* grad_scale;
   int64_t wait_ticks;  // bound of every wait on another wave, in wall_clock64() ticks
 };
+
+// grad_scale[b] in the loss type of the input dtype (float64 for float64 inputs, else float32), or 1
+__device__ __forceinline__ double grad_scale_of(const Inputs& in, int64_t b) {
+  if (!in.grad_scale) return 1.0;
+  return in.dtype == kF64 ? static_cast<const double*>(in.grad_scale)[b] : (double)static_cast<const float*>(in.grad_scale)[b];
+}
+
+// The gradient weight of utterance b in float64 (the float64 path): as utterance_weight below.
+__device__ __forceinline__ double utterance_weight64(const Inputs& in, int64_t B, int64_t b, bool infinite) {
+  const int64_t U = load_index(in.target_lengths, in.index_flags & 8, b);
+  double w = grad_scale_of(in, b);
+  if (in.reduction == 2) w /= (double)B * (U > 1 ? (double)U : 1.0);
+  if (in.zero_infinity && infinite) w = 0.0;
+  return w;
+}
 
 // The gradient weight of utterance b: grad_scale[b] (or 1), over B * max(U, 1) for the mean (U as
 // the caller gave it), and 0 under zero_infinity for an utterance without alignment.
 __device__ __forceinline__ float utterance_weight(const Inputs& in, int64_t B, int64_t b, bool infinite) {
   const int64_t U = load_index(in.target_lengths, in.index_flags & 8, b);
   const double Uc = U > 1 ? (double)U : 1.0;
-  double w = in.grad_scale ? (double)in.grad_scale[b] : 1.0;
+  double w = grad_scale_of(in, b);
   if (in.reduction == 2) w /= (double)B * Uc;
   if (in.zero_infinity && infinite) w = 0.0;
   return static_cast<float>(w);
@@ -436,7 +451,7 @@ constexpr int64_t kHmmMaxTable = 16384;  // S * O floats of the emission table i
 
 // store: keep alpha, beta and the block offsets for the posteriors (false: the loss only)
 hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, int group, bool store, hipStream_t s);
-hipError_t launch_weights(const Inputs& in, const Layout& L, const Pointers& P, float* losses_out, float* reduced_out,
+hipError_t launch_weights(const Inputs& in, const Layout& L, const Pointers& P, void* losses_out, void* reduced_out,
                           hipStream_t s);
 hipError_t launch_classes(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
 hipError_t launch_posteriors(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s);
@@ -445,6 +460,11 @@ hipError_t launch_dense(const Inputs& in, const Layout& L, const Pointers& P, vo
 // recursions and, as their frames become ready, the posteriors and gradient rows
 bool stream_fits(const Inputs& in, const Layout& L);
 hipError_t launch_stream(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s);
+// float64 inputs in float64 arithmetic (f64.hip): alpha of every utterance (stored in the state region
+// as float64) and its loss; then beta with each frame's posteriors and gradient row (needs the
+// weights and the class maps)
+hipError_t launch_f64_alpha(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
+hipError_t launch_f64_beta_rows(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s);
 // zero gradient rows owned by no utterance
 hipError_t launch_gaps(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s);
 hipError_t launch_reduce(const float* losses, const void* target_lengths, bool i64, int64_t B, int reduction, float* out,

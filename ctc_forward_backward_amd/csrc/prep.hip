@@ -216,8 +216,8 @@ __global__ void __launch_bounds__(256) classes_kernel(Layout L, Pointers P) {
 
 // Losses after zero_infinity, gradient weights and the sum / mean reduction (one workgroup,
 // a fixed summation tree so that the reduced value is reproducible).
-__global__ void __launch_bounds__(256) weights_kernel(Inputs in, Layout L, Pointers P, float* losses_out,
-                                                      float* reduced_out) {
+__global__ void __launch_bounds__(256) weights_kernel(Inputs in, Layout L, Pointers P, void* losses_out,
+                                                      void* reduced_out) {
   __shared__ double part[256];
   double acc = 0.0;
   const int64_t B = L.B;
@@ -228,11 +228,14 @@ __global__ void __launch_bounds__(256) weights_kernel(Inputs in, Layout L, Point
     const double nll = broken ? (double)NAN : P.nll[b];
     const bool inf = nll == (double)INFINITY;
     const double loss = (in.zero_infinity && inf) ? 0.0 : nll;
-    if (losses_out) losses_out[b] = static_cast<float>(loss);
+    if (losses_out) {  // in the loss type of the input dtype: float64 for float64 inputs, else float32
+      if (in.dtype == kF64) static_cast<double*>(losses_out)[b] = loss;
+      else static_cast<float*>(losses_out)[b] = static_cast<float>(loss);
+    }
     // the target length of the reductions is the caller's value, as the page's reductions divide by it
     int64_t U = load_index(in.target_lengths, in.index_flags & 8, b);
     const double Uc = U > 1 ? (double)U : 1.0;
-    double w = in.grad_scale ? (double)in.grad_scale[b] : 1.0;
+    double w = grad_scale_of(in, b);
     if (in.reduction == 2) w /= (double)B * Uc;
     if (in.zero_infinity && inf) w = 0.0;
     P.w[b] = static_cast<float>(w);
@@ -247,7 +250,9 @@ __global__ void __launch_bounds__(256) weights_kernel(Inputs in, Layout L, Point
   if (threadIdx.x == 0 && reduced_out && in.reduction != 0) {
     double v = part[0];
     if (in.reduction == 2) v = B > 0 ? v / (double)B : (double)NAN;
-    *reduced_out = static_cast<float>(broken ? (double)NAN : v);
+    if (broken) v = (double)NAN;
+    if (in.dtype == kF64) *static_cast<double*>(reduced_out) = v;
+    else *static_cast<float*>(reduced_out) = static_cast<float>(v);
   }
 }
 
@@ -630,7 +635,7 @@ hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P,
   return hipGetLastError();
 }
 
-hipError_t launch_weights(const Inputs& in, const Layout& L, const Pointers& P, float* losses_out, float* reduced_out,
+hipError_t launch_weights(const Inputs& in, const Layout& L, const Pointers& P, void* losses_out, void* reduced_out,
                           hipStream_t s) {
   weights_kernel<<<1, 256, 0, s>>>(in, L, P, losses_out, reduced_out);
   return hipGetLastError();

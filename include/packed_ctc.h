@@ -33,9 +33,10 @@
 extern "C" {
 #endif
 
-/* log_probs / grad dtypes ([PR] `PACKED_CTC_LOSS_DTYPES`: float32, bfloat16, float16; the page sends
- * float64 to the padded path).  F64 is this library's own addition: float64 log probs are read as
- * float64 and carried in float32 arithmetic like the others; the gradient is written as float64. */
+/* log_probs / grad dtypes ([PR] `PACKED_CTC_LOSS_DTYPES`: float32, bfloat16, float16, computed in
+ * float32; the page sends float64 to the padded path, which keeps float64 precision).  F64 is this
+ * library's own addition: float64 log probs are computed in float64 throughout (recursions,
+ * posteriors, gradient), on the packed layout; it is the precision path, not a fast one. */
 #define PCTC_DTYPE_F32 0
 #define PCTC_DTYPE_BF16 1
 #define PCTC_DTYPE_F16 2
@@ -98,14 +99,16 @@ int packed_ctc_max_target_length(const void* target_lengths, int index_flags, in
  * extended label sequence blank, l1, blank, ..., lU, blank (S = 2U + 1 states):
  *   nll_b = -log(sum over alignments) by the log-space alpha recursion; T = 0 gives 0 when U = 0
  *           and +inf otherwise; no alignment gives +inf;
- *   losses_out[b] = nll_b, or 0 when zero_infinity and nll_b = +inf          (B floats, fp32);
- *   reduced_out   = sum_b losses_out[b] (SUM) or mean_b losses_out[b] / max(U_b, 1) (MEAN);
- *                   not written for NONE; may be NULL;
+ *   losses_out[b] = nll_b, or 0 when zero_infinity and nll_b = +inf   (B values of the loss type:
+ *                   float32 for F32 / BF16 / F16 inputs, float64 for F64 inputs);
+ *   reduced_out   = sum_b losses_out[b] (SUM) or mean_b losses_out[b] / max(U_b, 1) (MEAN), one
+ *                   value of the loss type; not written for NONE; may be NULL;
  *   grad_out      = (T_total, D) in the dtype of log_probs, round-to-nearest-even:
  *                   w_b * (exp(log_probs) - posterior summed per class) on the rows of utterance b,
  *                   0 on rows owned by no utterance.  This is the gradient with respect to the
  *                   logits of a log_softmax ([PR] module description).  w_b is
- *                   (grad_scale ? grad_scale[b] : 1) times 1/(B * max(U_b, 1)) for MEAN, and 0
+ *                   (grad_scale ? grad_scale[b] : 1; B values of the loss type, like
+ *                   losses_out) times 1/(B * max(U_b, 1)) for MEAN, and 0
  *                   when zero_infinity and nll_b = +inf.  An infeasible utterance with w_b != 0
  *                   gets NaN in every column of its rows.  May be NULL (loss only).
  *
@@ -128,7 +131,7 @@ int packed_ctc_max_target_length(const void* target_lengths, int index_flags, in
 int packed_ctc_loss(const void* log_probs, int dtype, int64_t T_total, int64_t D, const void* cu_seqlens,
                     const void* lengths, int64_t B, const void* targets, int64_t target_width,
                     const void* target_lengths, int index_flags, int64_t max_target_length, int blank,
-                    int zero_infinity, int reduction, const float* grad_scale, float* losses_out, float* reduced_out,
+                    int zero_infinity, int reduction, const void* grad_scale, void* losses_out, void* reduced_out,
                     void* grad_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -155,13 +158,13 @@ int packed_ctc_loss(const void* log_probs, int dtype, int64_t T_total, int64_t D
 int packed_ctc_forward(const void* log_probs, int dtype, int64_t T_total, int64_t D, const void* cu_seqlens,
                        const void* lengths, int64_t B, const void* targets, int64_t target_width,
                        const void* target_lengths, int index_flags, int64_t max_target_length, int blank,
-                       int zero_infinity, int reduction, float* losses_out, float* reduced_out, void* workspace,
+                       int zero_infinity, int reduction, void* losses_out, void* reduced_out, void* workspace,
                        size_t workspace_bytes, void* stream);
 
 int packed_ctc_backward(const void* log_probs, int dtype, int64_t T_total, int64_t D, const void* cu_seqlens,
                         const void* lengths, int64_t B, const void* targets, int64_t target_width,
                         const void* target_lengths, int index_flags, int64_t max_target_length, int blank,
-                        int zero_infinity, int reduction, const float* grad_scale, void* grad_out, void* workspace,
+                        int zero_infinity, int reduction, const void* grad_scale, void* grad_out, void* workspace,
                         size_t workspace_bytes, void* stream);
 
 /*

@@ -27,7 +27,8 @@ from ctc_forward_backward_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-TOL = {torch.float32: (1e-4, 1e-4), torch.bfloat16: (2e-3, 2e-3), torch.float16: (2e-3, 2e-3)}
+TOL = {torch.float32: (1e-4, 1e-4), torch.bfloat16: (2e-3, 2e-3), torch.float16: (2e-3, 2e-3),
+       torch.float64: (1e-10, 1e-10)}
 
 
 def _say(*a):
@@ -58,7 +59,8 @@ def _check_oracle(losses, grad, ref, dtype, label):
     rloss = ref["loss"]
     assert np.array_equal(np.isinf(loss), np.isinf(rloss)), label
     fin = ~np.isinf(rloss)
-    np.testing.assert_allclose(loss[fin], rloss[fin], rtol=lrt, atol=1e-5, err_msg=label)
+    np.testing.assert_allclose(loss[fin], rloss[fin], rtol=lrt, atol=0 if dtype == torch.float64 else 1e-5,
+                               err_msg=label)
     if grad is not None:
         g = grad.detach().cpu().double().numpy()
         rg = ref["grad"]
@@ -328,3 +330,33 @@ def test_graph_replay_new_metadata_autograd(api, oracle_mod):
         torch.cuda.synchronize()
         ref = _oracle_for(oracle_mod, b.log_probs, b.cu_seqlens, ntg, ntl, nln)
         _check_oracle(out, lp.grad, ref, torch.float32, f"autograd replay {k} U={ntl.tolist()} T={nln.tolist()}")
+
+
+@pytest.mark.parametrize("reduction", ["none", "mean"])
+def test_float64_autograd_vs_oracle(api, oracle_mod, reduction):
+    """float64 log probs through autograd: losses (float64) and the gradient with upstream weights,
+    computed in float64, within 1e-10 of the oracle."""
+    _say(f"[gpu autograd] float64 ctc_loss.backward, reduction {reduction}")
+    rng = np.random.default_rng(41)
+    lengths = [int(x) for x in rng.integers(1, 300, size=9)] + [0]
+    tl = [int(rng.integers(0, max(1, T // 3) + 1)) for T in lengths]
+    tl[-1] = 0
+    targets = [[int(x) for x in rng.integers(1, 60, size=u)] for u in tl]
+    b = W.make_batch(lengths, targets, 60, seed=41, sigma=2.0, dtype="f64", reduction=reduction)
+    lp = b.log_probs.to("cuda:0").requires_grad_(True)
+    out = api.ctc_loss(lp, *_dev_args(b), blank=b.blank, reduction=reduction)
+    assert out.dtype == torch.float64
+    if reduction == "none":
+        g = torch.linspace(-1.0, 1.0, b.B, dtype=torch.float64, device="cuda:0")
+        out.backward(g)
+        gs = g.cpu().numpy()
+    else:
+        out.backward(torch.tensor(0.75, dtype=torch.float64, device="cuda:0"))
+        gs = np.full(b.B, 0.75)
+    torch.cuda.synchronize()
+    ref = oracle_mod.ctc_batch(b, reduction=reduction, grad_scale=gs)
+    losses = out if reduction == "none" else torch.from_numpy(ref["loss"])
+    _check_oracle(losses, lp.grad, ref, torch.float64, f"float64 autograd/{reduction}")
+    if reduction != "none":
+        np.testing.assert_allclose(float(out.detach().cpu()), ref["reduced"], rtol=1e-10, atol=0)
+    assert lp.grad.dtype == torch.float64

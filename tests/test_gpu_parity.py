@@ -1,7 +1,7 @@
 """HIP path vs the float64 oracle, element by element, through the C ABI.
 
-Tolerances: losses within 1e-4 relative for float32 (and float64, carried in float32 arithmetic)
-inputs and 2e-3 for bfloat16 / float16 inputs;
+Tolerances: losses within 1e-4 relative for float32 inputs, 2e-3 for bfloat16 / float16 inputs and
+1e-10 for float64 inputs (computed in float64);
 gradients within 1e-4 / 2e-3 absolute (the gradient is stored in the input dtype, so for bfloat16 /
 float16 the rounding of the stored value is part of the budget).  Several results are correct where
 the method sums repeated labels in any order; the comparison is tolerance-based throughout.
@@ -17,7 +17,9 @@ from ctc_forward_backward_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-TOL = {torch.float32: (1e-4, 1e-4), torch.float64: (1e-4, 1e-4), torch.bfloat16: (2e-3, 2e-3),
+# float64 inputs are computed in float64: the precision the page's float64 path keeps (its test of
+# that path compares at 1e-10)
+TOL = {torch.float32: (1e-4, 1e-4), torch.float64: (1e-10, 1e-10), torch.bfloat16: (2e-3, 2e-3),
        torch.float16: (2e-3, 2e-3)}
 
 
@@ -68,9 +70,11 @@ def compare(got, ref, dtype, label=""):
     inf_ref = np.isinf(rloss)
     assert np.array_equal(np.isinf(loss), inf_ref), label
     fin = ~inf_ref
-    np.testing.assert_allclose(loss[fin], rloss[fin], rtol=lrt, atol=1e-5, err_msg=label)
+    np.testing.assert_allclose(loss[fin], rloss[fin], rtol=lrt, atol=0 if dtype == torch.float64 else 1e-5,
+                               err_msg=label)
     if ref.get("reduced") is not None and got.get("reduced") is not None:
-        np.testing.assert_allclose(got["reduced"], ref["reduced"], rtol=lrt, atol=1e-6, err_msg=label)
+        # (the reduced value and the losses are stored as float32 for every input dtype)
+        np.testing.assert_allclose(got["reduced"], ref["reduced"], rtol=max(lrt, 1e-7), atol=1e-6, err_msg=label)
     if got.get("grad") is not None:
         g, rg = got["grad"], ref["grad"]
         nan_ref = np.isnan(rg)
@@ -317,8 +321,8 @@ def test_repeatable_within_tolerance(api):
 
 @pytest.mark.parametrize("reduction", ["none", "mean"])
 def test_float64_inputs(api, oracle_mod, reduction):
-    """float64 log probs, read as float64, carried in float32 arithmetic, gradient written as float64:
-    the float32 tolerances; several tiles of a 1025-class row and a ragged tail."""
+    """float64 log probs computed in float64 throughout, gradient written as float64: 1e-10 against the
+    oracle; several tiles of a 1025-class row and a ragged tail."""
     _say(f"[gpu parity] float64 inputs, reduction {reduction}")
     rng = np.random.default_rng(31)
     lengths = [int(x) for x in rng.integers(1, 400, size=11)] + [0, 3]

@@ -129,7 +129,7 @@ def main():
     W_ = int(b.targets.shape[1])
     flags = 1 * (cu.dtype == torch.int64) | 2 * (ln.dtype == torch.int64) | 4 * (tg.dtype == torch.int64) \
         | 8 * (tl.dtype == torch.int64)
-    ws_bytes = api.packed_ctc_workspace_size(T_total, D, B, Umax)
+    ws_bytes = api.packed_ctc_workspace_size(T_total, D, B, Umax, 1)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     losses = torch.empty(B, dtype=torch.float32, device=dev)
     reduced = torch.empty((), dtype=torch.float32, device=dev)
@@ -139,7 +139,7 @@ def main():
     sh = ctypes.c_void_p(stream.cuda_stream)
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
     call_args = (P(lp), api.DTYPE_CODES[lp.dtype], T_total, D, P(cu), P(ln), B, P(tg), W_, P(tl), flags, Umax,
-                 b.blank, int(b.zero_infinity), red_code, None, P(losses), P(reduced), P(grad), P(ws), ws_bytes, sh)
+                 b.blank, int(b.zero_infinity), red_code, None, P(losses), P(reduced), P(grad), 1, P(ws), ws_bytes, sh)
 
     def step():
         rc = lib.packed_ctc_loss(*call_args)

@@ -193,7 +193,9 @@ struct Ctx {
   int* prog_cons;
   int* prog_self;
   int* sig;                 // this block's per-lane offsets of the utterance's chunk 0 (64 ints per chunk)
-  float* ab;                // this block's 128 states per row (row 0)
+  float* ab;                // this block's 128 states per row (row 0), or (ck) per kept step (slot 0)
+  bool ck;                  // alpha kept only every K-th step (the grouped pipeline's checkpointing)
+  int lk;                   // log2 K
   bool store;               // keep the states and offsets (false: loss only, nothing is written)
   int* prog;                // streamed pipeline, the chain's last block: where it publishes its stored steps
   int* err;
@@ -201,6 +203,13 @@ struct Ctx {
   const Inputs* in;
   int64_t B;
 };
+
+// a 64-bit value the caller knows to be the same in every lane, moved to scalar registers
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 
 // vmcnt(62) with the other counters left alone (gfx9 s_waitcnt encoding: vmcnt bits 3:0 and 15:14,
 // expcnt 6:4, lgkmcnt 11:8)
@@ -271,7 +280,7 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{__builtin_bit_cast(uint32_t, v0.x), __builtin_bit_cast(uint32_t, v0.y)},
                                               ab0, lane * 8, 0, kStoreSc1);
       } else {
-        *reinterpret_cast<float2*>(cx.ab + r * 128 + 2 * lane) = v0;
+        *reinterpret_cast<float2*>(cx.ab + (cx.ck ? 0 : r * 128) + 2 * lane) = v0;  // step 0 is always kept
       }
     }
     if (lane == edge) {
@@ -337,9 +346,14 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
       // the producer's values in the offset of the lane that takes them
       const float hv = slot_value(raw, lanef(off, edge_in));
       const float shift = lane_shift(off);
-      // loss only: a resource of no bytes, so the hardware discards the per-frame stores (range check)
-      const __amdgpu_buffer_rsrc_t ab = __builtin_amdgcn_make_buffer_rsrc(cx.ab + chunk_lo(c) * 128, 0,
-                                                                          cx.store ? kK * 512 : 0, kRsrcWord3);
+      // loss only: a resource of no bytes, so the hardware discards the per-frame stores (range check).
+      // Checkpointing (alpha, grouped pipeline): the chunk's kept steps 32c + K, 32c + 2K, ... go to
+      // consecutive slots; the other frames' stores fall outside the resource and are discarded.
+      const bool ck = !BETA && !STREAM && cx.ck;
+      const int64_t abase = ck ? (((int64_t)c * kK >> cx.lk) + 1) * 128 : chunk_lo(c) * 128;
+      const int arec = cx.store ? (ck ? (kK >> cx.lk) * 512 : kK * 512) : 0;
+      const __amdgpu_buffer_rsrc_t ab = __builtin_amdgcn_make_buffer_rsrc(cx.ab + abase, 0, arec, kRsrcWord3);
+      const int kmask = (1 << cx.lk) - 1;
       const __amdgpu_buffer_rsrc_t er = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float*>(P.E + chunk_lo(c + 1) * Es), 0, static_cast<int>(kK * Es * 4), kRsrcWord3);
       const uint32_t hi = slot_hi(off, c);
@@ -370,7 +384,8 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
         xl = nl;
         const u32x2 st = BETA ? u32x2{__builtin_bit_cast(uint32_t, pl), __builtin_bit_cast(uint32_t, t)}
                               : u32x2{__builtin_bit_cast(uint32_t, xb), __builtin_bit_cast(uint32_t, xl)};
-        __builtin_amdgcn_raw_buffer_store_b64(st, ab, lane * 8, in_chunk(i) * 512, STREAM ? kStoreSc1 : 0);
+        const int so = !ck ? in_chunk(i) * 512 : (((i + 1) & kmask) == 0 ? (((i + 1) >> cx.lk) - 1) * 512 : 0x40000000);
+        __builtin_amdgcn_raw_buffer_store_b64(st, ab, lane * 8, so, STREAM ? kStoreSc1 : 0);
         if (lane == edge) {
           const unsigned long long v = pack(xl, hi);
           if (OUT_GLOBAL) gstore(gslot + drow * i, v);
@@ -475,7 +490,13 @@ __device__ __forceinline__ void run_wave(const Inputs& in, const Layout& L, cons
   cx.prog_cons = &sh.prog[beta ? max(w - 1, 0) : min(w + 1, kWaves - 1)];
   cx.prog_self = &sh.prog[w];
   cx.sig = P.sig + ((dir * Gm + j) * L.NCH + P.cbase[cx.b]) * 64;
-  cx.ab = P.AB + (dir * Gm + j) * TT * 128;
+  // beta: row-indexed; alpha: row-indexed, or (checkpointing) the utterance's kept steps.  The base is
+  // one offset from the alpha table, made explicitly uniform: the per-frame stores take it as a
+  // buffer resource, which must sit in scalar registers
+  cx.ck = !STREAM && !beta && L.K > 1;
+  cx.lk = __builtin_ctz(static_cast<unsigned>(L.K));
+  const int64_t abo = beta ? (Gm * L.NQ + j * TT) * 128 : (cx.ck ? (j * L.NQ + P.qbase[cx.b]) * 128 : j * TT * 128);
+  cx.ab = P.ABa + uniform64(abo);
   cx.store = store;
   cx.prog = (STREAM && (beta ? j == 0 : j == G - 1)) ? P.prog + chain : nullptr;
   cx.err = &P.ctl->err;

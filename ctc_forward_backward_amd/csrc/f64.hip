@@ -104,7 +104,7 @@ __global__ void __launch_bounds__(kT64) f64_alpha_kernel(Inputs in, Layout L, Po
   const bool active = tid < sp.n;
   const int cnt = active ? sp.hi - sp.lo : 0;
   const int64_t Ss = L.Gmax * 128, D = L.D;
-  double* A = reinterpret_cast<double*>(P.AB);
+  double* A = reinterpret_cast<double*>(P.ABa);
   int cls[kPer64];
   bool skip[kPer64];
   double a[kPer64];
@@ -193,7 +193,7 @@ __global__ void __launch_bounds__(kT64) f64_beta_rows_kernel(Inputs in, Layout L
   const Split sp = split_of(S, tid);
   const bool active = tid < sp.n;
   const int cnt = active ? sp.hi - sp.lo : 0;
-  const double* A = reinterpret_cast<const double*>(P.AB);
+  const double* A = reinterpret_cast<const double*>(P.ABa);
   int cls[kPer64], rank[kPer64];
   bool skip[kPer64];
   double bt[kPer64];

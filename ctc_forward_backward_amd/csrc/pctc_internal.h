@@ -59,7 +59,9 @@ struct Layout {
   int64_t Dw;        // 32-bit words of a class bitmap: ceil(D / 32)
   int64_t C_stride;  // floats per row of the compact class sums (>= Umax + 1)
   int64_t NCH;       // chunk slots of the per-lane offsets: >= sum over utterances of ceil((T - 1) / kChunk)
-  size_t off_cbase, off_cbits, off_cpref, off_dmap, off_meta, off_lab, off_rowmap, off_rowoff, off_E, off_Eb, off_AB, off_nll, off_llb, off_lsh, off_w, off_post, off_order, off_cum, off_ring,
+  int64_t K;         // checkpoint interval of alpha: every K-th step kept (1: every step)
+  int64_t NQ;        // alpha rows kept per block: T_total (K = 1), else >= sum over utterances of ceil(T / K)
+  size_t off_qbase, off_cbase, off_cbits, off_cpref, off_dmap, off_meta, off_lab, off_rowmap, off_rowoff, off_E, off_Eb, off_AB, off_nll, off_llb, off_lsh, off_w, off_post, off_order, off_cum, off_ring,
       off_sig, off_items, off_ctl, off_prog, off_bands, total;
 };
 
@@ -99,7 +101,9 @@ constexpr int kBand = 16;
 // workgroup of the streamed pipeline: four recursion waves (one per SIMD), or sixteen row waves
 constexpr int kStreamWaves = 16;
 
-Layout make_layout(int64_t T_total, int64_t D, int64_t B, int64_t Umax);
+Layout make_layout(int64_t T_total, int64_t D, int64_t B, int64_t Umax, int64_t K = 1);
+constexpr int kMaxCheckpoint = 32;        // checkpoint intervals: powers of two up to the chunk
+constexpr int kMaxCheckpointBlocks = 16;  // checkpointed utterances: up to 16 state blocks (U <= 1023)
 
 struct Pointers {
   Meta* meta;
@@ -108,11 +112,16 @@ struct Pointers {
   int* rowoff;   // (T_total,): integer offset subtracted from the row's gathered log2 emissions
   float* E;      // (T_total, E_stride): columns 0..U the labels, U+1 holds -1e30; kEPad rows of padding on either side
   float* Eb;     // (T_total,): column 0 of E (the blank) again, contiguous for the recursions; kEPad padding each side
-  // (2, Gmax, T_total, 128): normalised log2 alpha (direction 0) and beta (direction 1) per block
-  // of 64 state pairs and per row.  Alpha pair k sits at 2k, 2k+1 (states 2k, 2k+1); beta pair k at
-  // 2k, 2k+1 (states 2k-1, 2k), i.e. beta of state s at position s+1, each relative to its lane's
-  // offset for that chunk (sig).
-  float* AB;
+  // Normalised log2 alpha and beta per block of 64 state pairs and per row, 128 floats each.  Alpha
+  // pair k sits at 2k, 2k+1 (states 2k, 2k+1); beta pair k at 2k, 2k+1 (states 2k-1, 2k), i.e. beta
+  // of state s at position s+1, each relative to its lane's offset for that chunk (sig).
+  //   ABa: alpha, (Gmax, NQ, 128): K = 1 row-indexed (NQ = T_total); K > 1 the kept steps 0, K, 2K,
+  //        ... of utterance b at slots qbase[b] + step / K
+  //   ABb: beta, (Gmax, T_total, 128), row-indexed
+  // (K = 1: ABb follows ABa, and the float64 path uses the two as one float64 array)
+  float* ABa;
+  float* ABb;
+  int* qbase;    // (B + 1) first alpha slot of each utterance (K > 1: exclusive prefix of ceil(T / K))
   double* nll;   // (B,) raw negative log-likelihood in nats (+inf: no alignment)
   double* llb;   // (B,) log2 likelihood from the beta side (consistency check)
   double* lsh;   // (B,) log2 likelihood from the alpha side without the row offsets
@@ -465,6 +474,8 @@ hipError_t launch_stream(const Inputs& in, const Layout& L, const Pointers& P, v
 // weights and the class maps)
 hipError_t launch_f64_alpha(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
 hipError_t launch_f64_beta_rows(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s);
+// alpha checkpointing (ckpt.hip): every row's class sums from alpha recomputed out of the kept steps
+hipError_t launch_ckpt_posteriors(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
 // zero gradient rows owned by no utterance
 hipError_t launch_gaps(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s);
 hipError_t launch_reduce(const float* losses, const void* target_lengths, bool i64, int64_t B, int reduction, float* out,

@@ -335,12 +335,16 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
   const float share[kMaxGroups][kMaxGroups] = {{1.0f, 1.0f, 1.0f}, {0.15f, 1.0f, 1.0f}, {0.45f, 0.75f, 1.0f}};
   // first slot of each utterance's chunks in the per-lane offset table: chunk c holds steps
   // 1 + c kChunk .. (c + 1) kChunk, so an utterance of T frames has ceil((T - 1) / kChunk) chunks
+  // and, with alpha checkpointing (interval K), the first slot of each utterance's kept steps
+  // 0, K, 2K, ... <= T - 1
   for (int b = tid; b < B; b += nt) {
     const int T = P.meta[b].T;
     P.cbase[b] = T > 1 ? (T - 1 + kChunk - 1) / kChunk : 0;
+    P.qbase[b] = T > 0 ? (T - 1) / static_cast<int>(L.K) + 1 : 0;
   }
   __syncthreads();
   block_exclusive_scan(P.cbase, B, wsum);
+  block_exclusive_scan(P.qbase, B, wsum);
   if (sort) {
     int* sT = sh;
     int* order = sh + B;

@@ -88,13 +88,13 @@ __device__ __forceinline__ void posterior_row(const Layout& L, const Pointers& P
         const int ob1 = lane < 63 ? offB(j, lane + 1) : (j + 1 < G ? offB(j + 1, 0) : ob0);
         c0[u] = static_cast<float>((double)(oa + ob0) - lsh);
         c1[u] = static_cast<float>((double)(oa + ob1) - lsh);
-        const int64_t rb = ((Gm + j) * TT + r) * 128;
+        const int64_t rb = ((int64_t)j * TT + r) * 128;
         if (k <= U) {
-          a[u] = *reinterpret_cast<const float2*>(P.AB + ((int64_t)j * TT + r) * 128 + 2 * lane);
-          b0[u] = P.AB[rb + 2 * lane + 1];
+          a[u] = *reinterpret_cast<const float2*>(P.ABa + rb + 2 * lane);
+          b0[u] = P.ABb[rb + 2 * lane + 1];
         }
         if (k < U) {  // then for lane 63 the next block exists
-          b1[u] = P.AB[lane < 63 ? rb + 2 * lane + 2 : rb + TT * 128];
+          b1[u] = P.ABb[lane < 63 ? rb + 2 * lane + 2 : rb + TT * 128];
           d1[u] = dmap[k + 1];
         }
       }
@@ -177,14 +177,14 @@ __device__ __forceinline__ bool posterior_stream(const Layout& L, const Pointers
         // state 2k+1 takes beta (and its offset) from the next lane: lane 63 from the next block's lane 0
         const int jn = lane < 63 ? j : min(j + 1, G - 1), ln = lane < 63 ? lane + 1 : 0;
         const int oa = offA(j, lane), ob0 = offB(j, lane), ob1 = offB(jn, ln);
-        const int64_t rb = ((Gm + j) * TT + r) * 128;
+        const int64_t rb = ((int64_t)j * TT + r) * 128;
         c0[u] = oa + ob0 - ref;
         c1[u] = oa + ob1 - ref;
         if (k <= U) {
-          const float2 a = ld_dev2(P.AB + ((int64_t)j * TT + r) * 128 + 2 * lane);
-          s0[u] = a.x + ld_dev(P.AB + rb + 2 * lane + 1);
+          const float2 a = ld_dev2(P.ABa + rb + 2 * lane);
+          s0[u] = a.x + ld_dev(P.ABb + rb + 2 * lane + 1);
           if (k < U) {
-            s1[u] = a.y + ld_dev(P.AB + (lane < 63 ? rb + 2 * lane + 2 : rb + TT * 128));
+            s1[u] = a.y + ld_dev(P.ABb + (lane < 63 ? rb + 2 * lane + 2 : rb + TT * 128));
             d1[u] = dmap[k + 1];
           }
         }

@@ -71,10 +71,13 @@ extern "C" {
 #define PCTC_PIPELINE_STREAMED 1  /* one persistent launch: rows formed as the recursions pass them (default) */
 
 /*
- * Bytes of device workspace packed_ctc_loss needs for T_total frames, D classes, B utterances and
- * target lengths up to max_target_length.  Returns 0 for negative arguments.
+ * Bytes of device workspace a call needs for T_total frames, D classes, B utterances, target lengths
+ * up to max_target_length and alpha checkpoint interval checkpoint_interval (see packed_ctc_loss;
+ * 1 keeps every alpha row).  Returns 0 for negative sizes or an interval that is not a power of two
+ * in [1, 32].
  */
-size_t packed_ctc_workspace_size(int64_t T_total, int64_t D, int64_t B, int64_t max_target_length);
+size_t packed_ctc_workspace_size(int64_t T_total, int64_t D, int64_t B, int64_t max_target_length,
+                                 int checkpoint_interval);
 
 /*
  * Supported maxima of this build: the longest target (labels) and the class count D.
@@ -123,7 +126,14 @@ int packed_ctc_max_target_length(const void* target_lengths, int index_flags, in
  *   library's own (created on the first such call on a device, forked from and joined back into
  *   `stream` with events, so the call stays ordered on `stream` and is graph-capturable).  A call
  *   captured before that device's streams exist runs as one group on `stream`.
- * The workspace must be at least packed_ctc_workspace_size(T_total, D, B, bound) bytes, bound =
+ * checkpoint_interval K (a power of two in [1, 32]; [PR] `_alpha_kernel` keeps every alpha row):
+ *   alpha is kept for the steps 0, K, 2K, ... of each utterance only, and the rows of each K-step
+ *   interval recompute it from the kept step, so the alpha part of the workspace shrinks about
+ *   K-fold (beta is kept for every step).  K = 1 keeps every row.  K > 1 runs the grouped pipeline
+ *   (see packed_ctc_set_pipeline), takes float32 / bfloat16 / float16 inputs (PCTC_ERR_ARG for
+ *   float64) and target lengths up to 1023 (PCTC_ERR_LIMIT beyond).  Results agree with K = 1 to
+ *   float32 rounding.
+ * The workspace must be at least packed_ctc_workspace_size(T_total, D, B, bound, K) bytes, bound =
  *   max_target_length if >= 0 else target_width, and 256-byte aligned.
  * log_probs and grad_out must be 16-byte aligned (PCTC_ERR_ARG otherwise).
  * Rows of different utterances must not overlap.  Inputs are read only; outputs are fully written.
@@ -132,7 +142,7 @@ int packed_ctc_loss(const void* log_probs, int dtype, int64_t T_total, int64_t D
                     const void* lengths, int64_t B, const void* targets, int64_t target_width,
                     const void* target_lengths, int index_flags, int64_t max_target_length, int blank,
                     int zero_infinity, int reduction, const void* grad_scale, void* losses_out, void* reduced_out,
-                    void* grad_out, void* workspace, size_t workspace_bytes, void* stream);
+                    void* grad_out, int checkpoint_interval, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The same computation split at the autograd boundary ([PR] `_PackedCTCLoss.forward` stores alpha
@@ -147,8 +157,9 @@ int packed_ctc_loss(const void* log_probs, int dtype, int64_t T_total, int64_t D
  *   0 under zero_infinity for an infinite loss).  For autograd, grad_scale[b] is the upstream
  *   gradient of loss b (NONE), or the upstream scalar for every b (SUM, MEAN).
  *   Precondition: `workspace` holds the state of a packed_ctc_forward call on the same stream with
- *   the same log_probs, sizes, index arrays, blank and max_target_length (>= 0 here: it must be the
- *   bound the forward used; PCTC_ERR_ARG if negative), not reused by another call since.  The
+ *   the same log_probs, sizes, index arrays, blank, checkpoint_interval and max_target_length (>= 0
+ *   here: it must be the bound the forward used; PCTC_ERR_ARG if negative), not reused by another
+ *   call since.  The
  *   workspace is read, and only its weight, class-map and row-sum regions are rewritten, so the
  *   backward may be repeated with other grad_scale values.  zero_infinity and reduction may differ
  *   from the forward's; they only set the weights.
@@ -158,14 +169,14 @@ int packed_ctc_loss(const void* log_probs, int dtype, int64_t T_total, int64_t D
 int packed_ctc_forward(const void* log_probs, int dtype, int64_t T_total, int64_t D, const void* cu_seqlens,
                        const void* lengths, int64_t B, const void* targets, int64_t target_width,
                        const void* target_lengths, int index_flags, int64_t max_target_length, int blank,
-                       int zero_infinity, int reduction, void* losses_out, void* reduced_out, void* workspace,
-                       size_t workspace_bytes, void* stream);
+                       int zero_infinity, int reduction, void* losses_out, void* reduced_out,
+                       int checkpoint_interval, void* workspace, size_t workspace_bytes, void* stream);
 
 int packed_ctc_backward(const void* log_probs, int dtype, int64_t T_total, int64_t D, const void* cu_seqlens,
                         const void* lengths, int64_t B, const void* targets, int64_t target_width,
                         const void* target_lengths, int index_flags, int64_t max_target_length, int blank,
-                        int zero_infinity, int reduction, const void* grad_scale, void* grad_out, void* workspace,
-                        size_t workspace_bytes, void* stream);
+                        int zero_infinity, int reduction, const void* grad_scale, void* grad_out,
+                        int checkpoint_interval, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Reduction of per-utterance losses ([PR] `ctc.py` `forward_packed`): SUM = sum of losses[b];

@@ -65,8 +65,16 @@ def test_workspace_size():
     # the alpha and beta tables dominate: at least 2 * T_total * (2U + 2) floats
     assert a >= 2 * 1000 * 202 * 4
     lib = api._load()
-    assert lib.packed_ctc_workspace_size(-1, 5, 1, 1) == 0
-    assert lib.packed_ctc_workspace_size(5, 5, 1, -1) == 0
+    assert lib.packed_ctc_workspace_size(-1, 5, 1, 1, 1) == 0
+    assert lib.packed_ctc_workspace_size(5, 5, 1, -1, 1) == 0
+    assert lib.packed_ctc_workspace_size(5, 5, 1, 1, 3) == 0
+    assert lib.packed_ctc_workspace_size(5, 5, 1, 1, 64) == 0
+    # alpha checkpointing: the alpha part shrinks about K-fold; beta and the rest stay
+    full = f(32839, 8193, 16, 490)
+    k32 = f(32839, 8193, 16, 490, 32)
+    alpha = 8 * 32839 * 512  # Gmax = 8 blocks of 128 floats per row
+    assert full - k32 >= 0.9 * alpha
+    assert f(32839, 8193, 16, 490, 8) > k32
 
 
 def test_limits_and_version():
@@ -81,11 +89,12 @@ def _call(**kw):
     dummy = ctypes.c_void_p(0x1000)
     a = dict(log_probs=dummy, dtype=0, T_total=10, D=5, cu=dummy, lengths=dummy, B=2, targets=dummy, W=3,
              tl=dummy, flags=0, maxU=3, blank=0, zi=0, red=0, gs=None, losses=dummy, reduced=None, grad=None,
-             ws=None, ws_bytes=0, stream=None)
+             K=1, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return lib.packed_ctc_loss(a["log_probs"], a["dtype"], a["T_total"], a["D"], a["cu"], a["lengths"], a["B"],
                                a["targets"], a["W"], a["tl"], a["flags"], a["maxU"], a["blank"], a["zi"], a["red"],
-                               a["gs"], a["losses"], a["reduced"], a["grad"], a["ws"], a["ws_bytes"], a["stream"])
+                               a["gs"], a["losses"], a["reduced"], a["grad"], a["K"], a["ws"], a["ws_bytes"],
+                               a["stream"])
 
 
 @pytest.mark.parametrize("kw,code,needle", [
@@ -110,6 +119,11 @@ def _call(**kw):
     (dict(ws=None, ws_bytes=0), api.ERR_WORKSPACE, "workspace"),
     (dict(ws=ctypes.c_void_p(0x1000), ws_bytes=16), api.ERR_WORKSPACE, "workspace"),
     (dict(ws=ctypes.c_void_p(0x1001), ws_bytes=1 << 40), api.ERR_WORKSPACE, "aligned"),
+    (dict(K=3), api.ERR_ARG, "checkpoint_interval"),
+    (dict(K=64), api.ERR_ARG, "checkpoint_interval"),
+    (dict(K=0), api.ERR_ARG, "checkpoint_interval"),
+    (dict(K=8, dtype=3), api.ERR_ARG, "checkpointing"),
+    (dict(K=8, maxU=1024, W=1024), api.ERR_LIMIT, "checkpointing"),
 ])
 def test_host_checks(kw, code, needle):
     rc = _call(**kw)
@@ -141,13 +155,13 @@ def _split(which, **kw):
     dummy = ctypes.c_void_p(0x1000)
     a = dict(log_probs=dummy, dtype=0, T_total=10, D=5, cu=dummy, lengths=dummy, B=2, targets=dummy, W=3,
              tl=dummy, flags=0, maxU=3, blank=0, zi=0, red=0, gs=None, losses=dummy, reduced=None, grad=dummy,
-             ws=None, ws_bytes=0, stream=None)
+             K=1, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     head = (a["log_probs"], a["dtype"], a["T_total"], a["D"], a["cu"], a["lengths"], a["B"], a["targets"], a["W"],
             a["tl"], a["flags"], a["maxU"], a["blank"], a["zi"], a["red"])
     if which == "forward":
-        return lib.packed_ctc_forward(*head, a["losses"], a["reduced"], a["ws"], a["ws_bytes"], a["stream"])
-    return lib.packed_ctc_backward(*head, a["gs"], a["grad"], a["ws"], a["ws_bytes"], a["stream"])
+        return lib.packed_ctc_forward(*head, a["losses"], a["reduced"], a["K"], a["ws"], a["ws_bytes"], a["stream"])
+    return lib.packed_ctc_backward(*head, a["gs"], a["grad"], a["K"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("which,kw,code,needle", [

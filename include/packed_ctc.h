@@ -145,6 +145,26 @@ int packed_ctc_loss(const void* log_probs, int dtype, int64_t T_total, int64_t D
                     void* grad_out, int checkpoint_interval, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * packed_ctc_loss without a workspace argument, for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid hipMalloc).  Arguments and
+ * results as for packed_ctc_loss, with these differences:
+ *   - the workspace is a 128 MiB device array of the library's own, one per device, held from the
+ *     library's first use on that device until the process ends; a call whose workspace
+ *     (packed_ctc_workspace_size) exceeds 128 MiB fails with PCTC_ERR_WORKSPACE and launches nothing;
+ *   - max_target_length must be >= 0 (no host read; PCTC_ERR_ARG otherwise);
+ *   - the call runs on `stream` alone (one utterance group, no streams or events of the library).
+ * The call allocates nothing: no hipMalloc, hipFree or allocating library routine.  Every region of
+ * the array that a call's kernels read is written earlier in the same call, so nothing carries over
+ * from the previous call; calls that overlap on one device (other streams, other host threads)
+ * share the array and race: callers serialise them.
+ */
+int packed_ctc_loss_noalloc(const void* log_probs, int dtype, int64_t T_total, int64_t D, const void* cu_seqlens,
+                            const void* lengths, int64_t B, const void* targets, int64_t target_width,
+                            const void* target_lengths, int index_flags, int64_t max_target_length, int blank,
+                            int zero_infinity, int reduction, const void* grad_scale, void* losses_out,
+                            void* reduced_out, void* grad_out, int checkpoint_interval, void* stream);
+
+/*
  * The same computation split at the autograd boundary ([PR] `_PackedCTCLoss.forward` stores alpha
  * and the inputs; `_PackedCTCLoss.backward` runs beta and the gradient with the upstream
  * `grad_output`).

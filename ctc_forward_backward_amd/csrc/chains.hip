@@ -498,7 +498,7 @@ __device__ __forceinline__ void run_wave(const Inputs& in, const Layout& L, cons
   const int64_t abo = beta ? (Gm * L.NQ + j * TT) * 128 : (cx.ck ? (j * L.NQ + P.qbase[cx.b]) * 128 : j * TT * 128);
   cx.ab = P.ABa + uniform64(abo);
   cx.store = store;
-  cx.prog = (STREAM && (beta ? j == 0 : j == G - 1)) ? P.prog + chain : nullptr;
+  cx.prog = (STREAM && (beta ? j == 0 : j == G - 1)) ? P.prog + chain * kProgStride : nullptr;
   cx.err = &P.ctl->err;
   cx.ticks = in.wait_ticks;
   cx.in = &in;
@@ -580,8 +580,8 @@ __device__ __forceinline__ void row_band(const Inputs& in, const Layout& L, cons
   const int lo2 = T - 1 - re, hi2 = min(T - 1 - ra, ra - 1);        // and their mirrors
   const int n = n1 + max(hi2 - lo2 + 1, 0);
   if (w == 0) {
-    wait_steps(P.prog + 2 * b, re + 1, in.wait_ticks, &P.ctl->err);
-    wait_steps(P.prog + 2 * b + 1, re + 1, in.wait_ticks, &P.ctl->err);
+    wait_steps(P.prog + (2 * b) * kProgStride, re + 1, in.wait_ticks, &P.ctl->err);
+    wait_steps(P.prog + (2 * b + 1) * kProgStride, re + 1, in.wait_ticks, &P.ctl->err);
   }
   __syncthreads();  // (also keeps the compiler from moving the row's loads above the wait)
   if (w >= n) return;

@@ -98,6 +98,10 @@ struct ChainCtl {
 // [T/2 + k kBand, T/2 + (k+1) kBand): a band can be formed as soon as both recursions have passed
 // its last such step, so the bands of an utterance become ready from the middle frames outwards.
 constexpr int kBand = 16;
+// Each progress word sits on a cache line of its own (128 bytes): the bands of many utterances poll
+// them from every compute unit while the chains' last blocks write them, and words sharing lines
+// measured up to 55 us slower per call (asr_bpe).
+constexpr int kProgStride = 32;
 // workgroup of the streamed pipeline: four recursion waves (one per SIMD), or sixteen row waves
 constexpr int kStreamWaves = 16;
 
@@ -143,7 +147,7 @@ struct Pointers {
   // streamed pipeline: per (utterance, direction) the recursion steps whose states every block has
   // stored where any compute unit sees them, and the queue of row bands (utterance, band), readiest
   // first
-  int* prog;        // (2 B)
+  int* prog;        // (2 B) words, kProgStride ints apart
   int2* bands;      // (T_total / kBand + 2 B + 1): at most ceil(ceil(T/2) / kBand) <= T/64 + 2 per utterance
 };
 

@@ -504,7 +504,7 @@ __device__ void build_bands(const Layout& L, const Pointers& P, int* sT, int* fi
   __shared__ int bsum[16];
   __shared__ int tmax;
   if (tid == 0) tmax = 0;
-  for (int i = tid; i < 2 * B; i += nt) P.prog[i] = 0;
+  for (int i = tid; i < 2 * B; i += nt) P.prog[i * kProgStride] = 0;
   for (int b = tid; b < B; b += nt) first[b] = bands_of(sT[b]);
   __syncthreads();
   for (int b = tid; b < B; b += nt) atomicMax(&tmax, sT[b]);

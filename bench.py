@@ -29,7 +29,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "packed CTC loss+grad frames/s and achieved HBM GB/s (% of MI355X peak)"
 HBM_PEAK_GBPS = 8000.0
-FP32_VECTOR_PEAK_TFLOPS = 157.3
+# fp32 vector peak without packed FP32 instructions (the library is built without them): 256 compute
+# units x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz = 78.6 TFLOP/s (the packed rate is twice that)
+FP32_VECTOR_PEAK_TFLOPS = 78.6
+WORKLOADS = ["tiny", "small", "asr_bpe", "large_vocab", "char_level"]
 DTYPE_BYTES = {"f32": 4, "bf16": 2, "f16": 2}
 
 # fp32 operations charged per state and frame of one recursion (alpha or beta): a 3-way max/med/min,
@@ -73,6 +76,129 @@ def profiled_traffic(workload: str, phase: str):
     if sha != kernel_sources_sha() or len(rows) != 1:
         return None
     return next(iter(rows.values()))
+
+
+def _median_ms(stream, fn, n, warm=2):
+    import torch
+
+    for _ in range(warm):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    return t[len(t) // 2]
+
+
+def all_configs(api, lib, dev, stream):
+    """Every workload: median call time on the default (streamed) pipeline, frames/s, counted GB/s and
+    its fraction of 8 TB/s, the longest utterance's frames and ns per frame of the call; the
+    recursion floor (the longest utterance alone, loss only: its recursion kernel time) and the
+    critical-path fraction (that floor over the call); alpha checkpointing at K = 8 and 32 (grouped
+    pipeline): workspace and call time."""
+    import ctypes
+
+    import torch
+
+    from ctc_forward_backward_amd import workloads as W
+
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    res = {}
+    for name in WORKLOADS:
+        b = W.make_workload(name)
+        lp, cu, ln, tg, tl = (x.to(dev) for x in (b.log_probs, b.cu_seqlens, b.lengths, b.targets, b.target_lengths))
+        Umax, Wd = int(b.target_lengths.max()), int(b.targets.shape[1])
+        flags = 1 * (cu.dtype == torch.int64) | 2 * (ln.dtype == torch.int64) | 4 * (tg.dtype == torch.int64) \
+            | 8 * (tl.dtype == torch.int64)
+        losses = torch.empty(b.B, dtype=torch.float32, device=dev)
+        reduced = torch.empty((), dtype=torch.float32, device=dev)
+        grad = torch.empty((b.T_total, b.D), dtype=lp.dtype, device=dev)
+        bpe = lp.element_size()
+        counted = b.T_total * b.D * 2 * bpe
+        t_max = int(b.lengths.max())
+        entry = {"B": b.B, "T_total": b.T_total, "D": b.D, "input_dtype": str(lp.dtype).replace("torch.", ""),
+                 "T_max": t_max}
+        for K in (1, 8, 32):
+            ws_bytes = api.packed_ctc_workspace_size(b.T_total, b.D, b.B, Umax, K)
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+            args = (P(lp), api.DTYPE_CODES[lp.dtype], b.T_total, b.D, P(cu), P(ln), b.B, P(tg), Wd, P(tl), flags, Umax,
+                    b.blank, int(b.zero_infinity), api.REDUCTIONS[b.reduction], None, P(losses), P(reduced), P(grad),
+                    K, P(ws), ws_bytes, sh)
+
+            def call():
+                rc = lib.packed_ctc_loss(*args)
+                if rc != 0:
+                    raise RuntimeError(lib.packed_ctc_last_error().decode())
+
+            ms = _median_ms(stream, call, 10 if K == 1 else 5)
+            if K == 1:
+                gbps = counted / (ms * 1e-3) / 1e9
+                entry.update({"ms_per_call": ms, "frames_per_s": b.T_total / (ms * 1e-3), "counted_gbps": gbps,
+                              "hbm_frac": gbps / HBM_PEAK_GBPS, "ns_per_frame_of_T_max": ms * 1e6 / t_max,
+                              "workspace_bytes": ws_bytes})
+            else:
+                entry[f"checkpoint_K{K}"] = {"ms_per_call": ms, "workspace_bytes": ws_bytes}
+            del ws
+        # the recursion floor: the longest utterance alone, loss only, its recursion kernel's time
+        i = int(b.lengths.argmax())
+        r0, T0, U0 = int(b.cu_seqlens[i]), int(b.lengths[i]), int(b.target_lengths[i])
+        lp1 = lp[r0:r0 + T0].contiguous()
+        one = (torch.tensor([0, T0], dtype=torch.int32, device=dev), torch.tensor([T0], device=dev),
+               tg[i:i + 1].contiguous(), torch.tensor([U0], device=dev))
+        api.packed_ctc_loss(lp1, *one, blank=b.blank, need_grad=False, max_target_length=U0)
+        torch.cuda.synchronize()
+        api.set_phase_timing(True)
+        for _ in range(5):
+            api.packed_ctc_loss(lp1, *one, blank=b.blank, need_grad=False, max_target_length=U0)
+        torch.cuda.synchronize()
+        ph = api.phase_times()
+        api.set_phase_timing(False)
+        floor_ms = ph.get("chains@0", float("nan"))
+        entry["critical_path"] = {"frames": t_max, "labels": U0, "floor_us": floor_ms * 1e3,
+                                  "floor_ns_per_frame": floor_ms * 1e6 / t_max,
+                                  "call_frac": floor_ms / entry["ms_per_call"]}
+        res[name] = entry
+        del lp, grad
+        torch.cuda.empty_cache()
+    return res
+
+
+def extras(api, dev, stream):
+    """The autograd forward + backward on the large-vocabulary batch, and float64 inputs (computed in
+    float64) on a 13-utterance, 1025-class batch: median times."""
+    import numpy as np
+    import torch
+
+    from ctc_forward_backward_amd import workloads as W
+
+    out = {}
+    b = W.make_workload("large_vocab")
+    lp = b.log_probs.to(dev).requires_grad_(True)
+    args = tuple(x.to(dev) for x in (b.cu_seqlens, b.lengths, b.targets, b.target_lengths))
+    kw = dict(blank=b.blank, reduction=b.reduction, max_target_length=int(b.target_lengths.max()))
+
+    def fwd_bwd():
+        lp.grad = None
+        api.ctc_loss(lp, *args, **kw).backward()
+
+    out["autograd_large_vocab"] = {"ms_forward_backward": _median_ms(stream, fwd_bwd, 10),
+                                   "note": "ctc_loss(...).backward(): packed_ctc_forward + packed_ctc_backward"}
+    del lp
+    rng = np.random.default_rng(31)
+    lengths = [int(x) for x in rng.integers(1, 400, size=11)] + [0, 3]
+    tl = [int(rng.integers(0, max(1, T // 3) + 1)) for T in lengths]
+    targets = [[int(x) for x in rng.integers(1, 1025, size=u)] for u in tl]
+    b64 = W.make_batch(lengths, targets, 1025, seed=9, sigma=3.0, dtype="f64", reduction="mean")
+    a64 = tuple(x.to(dev) for x in (b64.log_probs, b64.cu_seqlens, b64.lengths, b64.targets, b64.target_lengths))
+    ms64 = _median_ms(stream, lambda: api.packed_ctc_loss(*a64, blank=0, reduction="mean",
+                                                          max_target_length=max(tl)), 10)
+    out["float64"] = {"workload": f"B={b64.B} T_total={b64.T_total} D=1025 float64, computed in float64",
+                      "ms_per_call": ms64, "frames_per_s": b64.T_total / (ms64 * 1e-3)}
+    return out
 
 
 def parse():
@@ -193,6 +319,7 @@ def main():
         t_max = int(lengths.max())
         t_crit = phases.get("chains@0", by_kernel["chains"]) * 1e-3
         roofline = {"bound": "alu", "kernel": "chains", "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                    "peak_note": "fp32 vector, non-packed (the library is built without packed FP32)",
                     "unit": "TFLOP/s", "frac": achieved / FP32_VECTOR_PEAK_TFLOPS,
                     "traffic": profiled_traffic(b.name, "chains"),
                     "work_per_call": f"2 recursions x {state_steps} state-steps x {OPS_PER_STATE_STEP} fp32 ops",
@@ -309,6 +436,14 @@ def main():
         out["hmm_forward"] = {"workload": f"S={hS} T={hT} B={hB} O={hO} float32", "us_per_call": h_us,
                               "sequences_per_s": hB / (h_us * 1e-6), "frames_per_s": hB * hT / (h_us * 1e-6),
                               "bound": "latency of T dependent log-semiring matrix-vector steps"}
+
+        out["configs"] = all_configs(api, lib, dev, stream)
+        out["extras"] = extras(api, dev, stream)
+        crit = out["configs"]["large_vocab"]["critical_path"] if b.name == "large_vocab" else None
+        if crit is not None and out["roofline"] is not None and "stream" in by_kernel:
+            # the launch's own floor: the longest recursion alone (loss-only call on that utterance)
+            out["roofline"]["critical_path"] = dict(crit, launch_us=by_kernel["stream"] * 1e3,
+                                                   frac=crit["floor_us"] / (by_kernel["stream"] * 1e3))
 
     if args.copy_calibration:  # last device work of the run
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)

@@ -438,7 +438,7 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
     const bool feasible = fin > kNegHalf;
     const double log2p = (double)rs + (double)off + (double)fin;
     if (!BETA) {
-      const bool nan = P.meta[cx.b].flags & 1;
+      const bool nan = P.meta[cx.b].flags & kNanInput;
       P.nll[cx.b] = nan ? (double)NAN : (feasible ? -log2p * kLn2 : (double)INFINITY);
       P.lsh[cx.b] = (double)off + (double)fin;
       P.w[cx.b] = utterance_weight(*cx.in, cx.B, cx.b, !nan && !feasible);  // for this group's rows
@@ -579,20 +579,21 @@ __device__ __forceinline__ void row_band(const Inputs& in, const Layout& L, cons
   const int n1 = re - ra + 1;                                       // frames ra .. re
   const int lo2 = T - 1 - re, hi2 = min(T - 1 - ra, ra - 1);        // and their mirrors
   const int n = n1 + max(hi2 - lo2 + 1, 0);
-  if (w == 0) {
+  if (w == 0 && !(m.flags & kNoAlignment)) {
     wait_steps(P.prog + (2 * b) * kProgStride, re + 1, in.wait_ticks, &P.ctl->err);
     wait_steps(P.prog + (2 * b + 1) * kProgStride, re + 1, in.wait_ticks, &P.ctl->err);
   }
   __syncthreads();  // (also keeps the compiler from moving the row's loads above the wait)
   if (w >= n) return;
   const bool broken = __builtin_amdgcn_readfirstlane(gave_up(&P.ctl->err));
-  const bool nan = m.flags & 1;
+  const bool nan = m.flags & kNanInput;
+  const bool none = m.flags & kNoAlignment;  // no alignment: its recursions are not run
   const float w0 = utterance_weight(in, L.B, b, false);
   float* acc = reinterpret_cast<float*>(lds);
   for (int i = w; i < n; i += kStreamWaves) {
     const int t = i < n1 ? ra + i : lo2 + (i - n1);
     const int64_t r = (int64_t)m.start + t;
-    if (!broken && !nan && w0 != 0.0f && rows::posterior_stream(L, P, acc, r, b, w0, lane)) {
+    if (!broken && !nan && !none && w0 != 0.0f && rows::posterior_stream(L, P, acc, r, b, w0, lane)) {
       rows::dense_row<DT, true>(in, L, P, grad, lds, r, b, w0, lane, cur_b);
     } else {
       const bool zero = !broken && (w0 == 0.0f || (!nan && in.zero_infinity));

@@ -31,8 +31,10 @@ struct Meta {
   int start;  // first row
   int T;      // frames (clamped so that rows stay inside the buffer)
   int U;      // labels (clamped to the workspace bound)
-  int flags;  // bit 0: a NaN log probability was gathered
+  int flags;  // kNanInput: a NaN log probability was gathered; kNoAlignment: T < U + repeats
 };
+constexpr int kNanInput = 1;
+constexpr int kNoAlignment = 2;
 
 // Workspace carve-up.  Every region is 256-byte aligned.
 // Frames per chunk of the recursions: their prefetch depth and the period of their integer shift.

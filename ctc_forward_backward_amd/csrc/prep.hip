@@ -67,10 +67,28 @@ __global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers
     lab[j] = static_cast<int>(c);
   }
   for (int t = threadIdx.x; t < mm.T; t += blockDim.x) P.rowmap[mm.start + t] = b;
+  // No alignment fits when the utterance has fewer frames than its labels need: one frame per label
+  // and a blank frame between two equal neighbours (the skip is barred between equal ids).  Such an
+  // utterance is marked here; its recursions are not run, since no state path reaches the end.
+  __shared__ int repeats;
+  if (threadIdx.x == 0) repeats = 0;
+  __syncthreads();  // (also: this workgroup's label writes above are visible to its loads below)
+  int rep = 0;
+  for (int j = threadIdx.x + 1; j < mm.U; j += blockDim.x) rep += lab[j + 1] == lab[j];
+  if (rep) atomicAdd(&repeats, rep);
+  __syncthreads();
+  if (threadIdx.x == 0 && mm.U > 0 && mm.T < mm.U + repeats) {
+    // what the recursions' owner blocks would record: an infinite loss and its weight (the gather
+    // turns both to those of a NaN loss if it meets a NaN at one of the utterance's columns)
+    P.meta[b].flags = kNoAlignment;
+    P.nll[b] = (double)INFINITY;
+    P.lsh[b] = 0.0;
+    P.llb[b] = -(double)INFINITY;
+    P.w[b] = utterance_weight(in, L.B, b, true);
+  }
   if (classes) {  // the class maps of this utterance (its labels were written above, by this workgroup)
     extern __shared__ uint32_t pcw[];
     __shared__ int wsum[4];
-    __syncthreads();
     class_maps(L, P, b, pcw, wsum);
   }
 }
@@ -149,7 +167,13 @@ __global__ void __launch_bounds__(256) gather_kernel(Inputs in, Layout L, Pointe
       E[U + 1] = kNeg;  // the column of label states that do not exist
       P.Eb[r] = E[0];   // (this lane wrote E[0] above)
     }
-    if (nan) atomicOr(&P.meta[b].flags, 1);
+    if (nan) {
+      atomicOr(&P.meta[b].flags, kNanInput);
+      if (P.meta[b].flags & kNoAlignment) {  // its loss is NaN, not +inf (no recursion will say so)
+        P.nll[b] = (double)NAN;
+        P.w[b] = utterance_weight(in, L.B, b, false);
+      }
+    }
   });
   if (gaps) {  // streamed pipeline: rows owned by no utterance get a zero gradient here
     const int64_t waves = (int64_t)gridDim.x * 4;
@@ -284,7 +308,8 @@ __global__ void __launch_bounds__(256) reduce_kernel(const float* losses, const 
 // which sits earlier in the queue, so segments claimed in queue order can always finish.
 // Frameless utterances get their loss here.
 constexpr int kBandBuckets = 4096;  // LDS buckets of 16 ready steps (a counting sort up to 65535 frames)
-__device__ void build_bands(const Layout& L, const Pointers& P, int* sT, int* first, int* hist, int nhist);
+__device__ void build_bands(const Layout& L, const Pointers& P, const int* sT, const int* sU, int* first, int* hist,
+                            int nhist);
 
 // exclusive prefix sum of a[0..n) in place, with a[n] = the total (one workgroup; every thread calls
 // it); wsum: blockDim / 64 words of LDS
@@ -326,7 +351,10 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
   __shared__ int gfirst[kMaxGroups + 1];
   const int B = static_cast<int>(L.B);
   const int tid = threadIdx.x, nt = blockDim.x;
-  auto nseg_of = [](int U) { return (((U + 1 + 63) >> 6) + kSegWaves - 1) / kSegWaves; };
+  // segments per direction; an utterance without alignment gets none (prep recorded its loss)
+  auto nseg_of = [](int U, int flags) {
+    return (flags & kNoAlignment) ? 0 : (((U + 1 + 63) >> 6) + kSegWaves - 1) / kSegWaves;
+  };
   // group g ends where the groups so far hold the share of the rows below (each group at least one
   // utterance); its segments in sorted order, each utterance's producers first.  With three
   // groups (cut points measured on uniformly spread lengths): the longest recursions with about
@@ -354,7 +382,7 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
     for (int b = tid; b < B; b += nt) {
       const Meta m = P.meta[b];
       sT[b] = m.T;
-      sU[b] = m.U;
+      sU[b] = (m.flags & kNoAlignment) ? -1 : m.U;  // -1: no alignment
     }
     __syncthreads();
     for (int b = tid; b < B; b += nt) {
@@ -371,7 +399,7 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
     for (int i = tid; i < B; i += nt) {
       const int b = order[i];
       cT[i] = sT[b];
-      cS[i] = sT[b] > 0 ? 2 * nseg_of(sU[b]) : 0;
+      cS[i] = sT[b] > 0 ? 2 * nseg_of(sU[b], sU[b] < 0 ? kNoAlignment : 0) : 0;
     }
     __syncthreads();
     block_exclusive_scan(cT, B, wsum);
@@ -418,7 +446,7 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
       while (g + 1 < groups && gfirst[g + 1] <= i) ++g;
       P.cum[i] = cT[i] - cT[gfirst[g]];
       if (sT[b] == 0) continue;
-      const int nseg = nseg_of(sU[b]);
+      const int nseg = nseg_of(sU[b], sU[b] < 0 ? kNoAlignment : 0);
       int n = cS[i];
       for (int j = 0; j < nseg; ++j) {
         P.items[n++] = ((2 * b) << 12) | j;
@@ -452,7 +480,7 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
             P.cum[i] = rows;
             rows += m.T;
             if (m.T == 0) continue;
-            const int nseg = nseg_of(m.U);
+            const int nseg = nseg_of(m.U, m.flags);
             for (int j = 0; j < nseg; ++j) {
               P.items[n++] = ((2 * i) << 12) | j;
               P.items[n++] = ((2 * i + 1) << 12) | (nseg - 1 - j);
@@ -477,7 +505,7 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
   }
   if (bands) {  // streamed pipeline (sorted, one group): the queue of row bands
     __syncthreads();
-    build_bands(L, P, sh, sh + 5 * B + 2, sh + 6 * B + 3, kBandBuckets);
+    build_bands(L, P, sh, sh + 2 * B, sh + 5 * B + 2, sh + 6 * B + 3, kBandBuckets);
   }
 }
 
@@ -497,8 +525,10 @@ __device__ __forceinline__ int bands_before(int T, int key) {
   return min(max((x + kBand - 1) / kBand - 1, 0), n);
 }
 
-// (one workgroup) sT: the frame counts (LDS, B); first: B + 1 words of LDS
-__device__ void build_bands(const Layout& L, const Pointers& P, int* sT, int* first, int* hist, int nhist) {
+// (one workgroup) sT: the frame counts (LDS, B); sU: the label counts, -1 for an utterance without
+// alignment, whose bands are ready at once and go first; first: B + 1 words of LDS
+__device__ void build_bands(const Layout& L, const Pointers& P, const int* sT, const int* sU, int* first, int* hist,
+                            int nhist) {
   const int B = static_cast<int>(L.B);
   const int tid = threadIdx.x, nt = blockDim.x;
   __shared__ int bsum[16];
@@ -520,7 +550,7 @@ __device__ void build_bands(const Layout& L, const Pointers& P, int* sT, int* fi
     }
     b = lo;
     k = i - first[b];
-    key = min(sT[b] / 2 + (k + 1) * kBand, sT[b]);
+    key = sU[b] < 0 ? 0 : min(sT[b] / 2 + (k + 1) * kBand, sT[b]);
   };
   const int nb = (tmax >> 4) + 1;  // buckets of 16 steps
   if (nb <= nhist) {
@@ -542,15 +572,19 @@ __device__ void build_bands(const Layout& L, const Pointers& P, int* sT, int* fi
     }
     return;
   }
-  // longer utterances: the exact order by ready step, ties by utterance, each band's place counted
+  // longer utterances: the exact order by ready step, ties by utterance (and by band within an
+  // utterance without alignment, all of whose bands are ready at step 0), each band's place counted
+  auto before = [&](int c, int key) {
+    return sU[c] < 0 ? (key > 0 ? bands_of(sT[c]) : 0) : bands_before(sT[c], key);
+  };
   for (int i = tid; i < N; i += nt) {
     int b, k, key;
     band_of(i, b, k, key);
-    int rank = 0;
+    int rank = sU[b] < 0 ? k : 0;
     for (int c = 0; c < B; ++c) {
-      const int before = bands_before(sT[c], key);
-      rank += before;
-      if (c < b) rank += bands_before(sT[c], key + 1) - before;  // a band of c ready at the same step
+      const int bf = before(c, key);
+      rank += bf;
+      if (c < b) rank += before(c, key + 1) - bf;  // a band of c ready at the same step
     }
     P.bands[rank] = make_int2(b, k);
   }

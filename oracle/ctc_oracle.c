@@ -38,7 +38,14 @@
  *   - an infeasible utterance with a non-zero weight (no zero_infinity) gets NaN in every column of
  *     its rows (the page's kernel would give NaN only at the blank and label columns; the padded
  *     library reference gives NaN everywhere);
- *   - the loss of a zero-frame utterance without labels is +0.0.
+ *   - the loss of a zero-frame utterance without labels is +0.0;
+ *   - a NaN log prob at a column the recursion reads (the blank or one of the utterance's labels) in
+ *     any of its rows makes the loss NaN, whether or not an alignment exists, and zero_infinity
+ *     leaves it (the loss is not infinite); its rows are then NaN in every column under a non-zero
+ *     weight.  A NaN at any other column leaves the loss alone and shows only in that column of
+ *     the gradient row.  (The page does not treat NaN inputs; torch's float64 ctc_loss gives the
+ *     same results wherever the NaN lies on a state some alignment can pass through.)
+ *   - a zero gradient weight gives zero rows, whatever the log probs hold.
  */
 #include <math.h>
 #include <stdint.h>
@@ -206,6 +213,10 @@ int ctc_oracle(const double* lp, int64_t T_total, int64_t D, const int64_t* cu, 
         if (T > 0 && (!alpha || !beta)) { free(alpha); free(beta); failed = 1; continue; }
         const double* ulp = lp + r * D;
         double n = utterance_alpha_beta(ulp, D, T, tgt, U, blank, alpha, beta);
+        /* reading: a NaN at the blank or a label column of an owned row makes the loss NaN */
+        for (int64_t t = 0; t < T && !isnan(n); ++t)
+            for (int64_t s = 0; s < S; ++s)
+                if (isnan(ulp[t * D + ext_label(tgt, s, blank)])) { n = NAN; break; }
         nll[b] = n;
         if (grad && T > 0) {
             /* step 6: the gradient weight of this utterance */
@@ -215,9 +226,9 @@ int ctc_oracle(const double* lp, int64_t T_total, int64_t D, const int64_t* cu, 
             for (int64_t t = 0; t < T; ++t) {
                 const double* row = ulp + t * D;
                 double* g = grad + (r + t) * D;
+                if (w == 0.0) continue; /* reading: a zero weight gives zero rows (left as cleared) */
                 for (int64_t c = 0; c < D; ++c) g[c] = w * exp(row[c]);
-                if (w == 0.0) continue;
-                if (isinf(n)) { /* reading: an infeasible utterance with a non-zero weight is NaN */
+                if (isinf(n) || isnan(n)) { /* readings: no alignment, or a NaN the recursion reads */
                     for (int64_t c = 0; c < D; ++c) g[c] = NAN;
                     continue;
                 }

@@ -7,6 +7,7 @@ float16 the rounding of the stored value is part of the budget).  Several result
 the method sums repeated labels in any order; the comparison is tolerance-based throughout.
 """
 
+import dataclasses
 import math
 
 import numpy as np
@@ -73,7 +74,7 @@ def compare(got, ref, dtype, label=""):
     np.testing.assert_allclose(loss[fin], rloss[fin], rtol=lrt, atol=0 if dtype == torch.float64 else 1e-5,
                                err_msg=label)
     if ref.get("reduced") is not None and got.get("reduced") is not None:
-        # (the reduced value and the losses are stored as float32 for every input dtype)
+        # (the reduced value and the losses are stored as float32, float64 for float64 inputs)
         np.testing.assert_allclose(got["reduced"], ref["reduced"], rtol=max(lrt, 1e-7), atol=1e-6, err_msg=label)
     if got.get("grad") is not None:
         g, rg = got["grad"], ref["grad"]
@@ -149,6 +150,54 @@ def test_zero_length_and_impossible(api, oracle_mod, zero_infinity):
     assert got["loss"][3] == (0.0 if zero_infinity else math.inf)  # T=1 with a repeat: no alignment
     if zero_infinity:
         assert np.all(got["grad"][8:9] == 0.0)
+
+
+def _boundary_batch(zero_infinity, reduction):
+    """Utterances one frame short of the fewest frames their labels need (U + repeats) beside ones
+    with exactly that many; equal neighbours, blank-id labels (blank 6), a 300-label target over
+    several state blocks; NaN log probs at the blank, at a label and at another column, with and
+    without an alignment."""
+    rng = np.random.default_rng(31)
+    long_t = [int(x) for x in rng.integers(1, 4, size=300)]
+    need = len(long_t) + sum(1 for i in range(1, len(long_t)) if long_t[i] == long_t[i - 1])
+    cases = [([1, 1, 2], 3), ([1, 1, 2], 4), ([3, 3, 3], 4), ([3, 3, 3], 5), ([6, 6, 1], 3), ([6, 6, 1], 4),
+             (long_t, need - 1), (long_t, need), ([2, 4], 9), ([2, 4], 9), ([1, 1, 2], 3), ([5], 7)]
+    targets = [t for t, _ in cases]
+    lengths = [T for _, T in cases]
+    b = W.make_batch(lengths, targets, 7, seed=32, sigma=1.5, blank=6, zero_infinity=zero_infinity,
+                     reduction=reduction)
+    lp = b.log_probs.clone()
+    cu = [int(x) for x in b.cu_seqlens]
+    lp[cu[8] + 4, 4] = float("nan")   # a label column, alignment exists
+    lp[cu[9] + 2, 6] = float("nan")   # the blank column, alignment exists
+    lp[cu[10] + 1, 2] = float("nan")  # a label column, no alignment
+    lp[cu[11] + 3, 0] = float("nan")  # a column no state reads
+    return dataclasses.replace(b, log_probs=lp)
+
+
+@pytest.mark.parametrize("zero_infinity", [False, True])
+def test_no_alignment_boundary_and_nan_inputs(api, oracle_mod, zero_infinity):
+    # an utterance with fewer frames than U + repeats runs no recursion (its loss is known to be
+    # +inf, or NaN with a NaN at a column the recursion reads); one with exactly that many aligns
+    _say(f"[gpu parity] no-alignment boundary and NaN inputs, zero_infinity={zero_infinity}")
+    for reduction in ("none", "mean"):
+        b = _boundary_batch(zero_infinity, reduction)
+        ref = oracle_mod.ctc_batch(b)
+        got = run_gpu(api, b)
+        compare(got, ref, torch.float32, f"boundary/{reduction}")
+        nll = ref["nll"]
+        assert np.isinf(nll[[0, 2, 4, 6]]).all() and np.isfinite(nll[[1, 3, 5, 7]]).all()
+        assert np.isnan(got["loss"][[8, 9, 10]]).all() and np.isfinite(got["loss"][11])
+    # and with alpha kept every 8th step (the grouped pipeline's checkpointed arrangement)
+    b = _boundary_batch(zero_infinity, "none")
+    dev = torch.device("cuda:0")
+    losses, _, grad = api.packed_ctc_loss(*(x.to(dev) for x in (b.log_probs, b.cu_seqlens, b.lengths, b.targets,
+                                                                b.target_lengths)),
+                                          blank=6, zero_infinity=zero_infinity, reduction="none",
+                                          checkpoint_interval=8)
+    torch.cuda.synchronize()
+    got = {"loss": losses.cpu().double().numpy(), "grad": grad.cpu().double().numpy()}
+    compare(got, oracle_mod.ctc_batch(b), torch.float32, "boundary K=8")
 
 
 def test_over_allocated_targets_fillers_and_gaps(api, oracle_mod):
@@ -236,7 +285,10 @@ def test_utterance_beyond_band_buckets(api, oracle_mod):
     lengths = [70000, 300]
     tl = [60, 20]
     targets = [[int(x) for x in rng.integers(1, 8, size=u)] for u in tl]
-    b = W.make_batch(lengths, targets, 8, seed=9, sigma=1.0, reduction="sum")
+    # and one without alignment (5 frames, 4 equal labels need 7), whose bands go first
+    lengths.append(5)
+    targets.append([3, 3, 3, 3])
+    b = W.make_batch(lengths, targets, 8, seed=9, sigma=1.0, reduction="sum", zero_infinity=True)
     ref = oracle_mod.ctc_batch(b)
     got = run_gpu(api, b)
     current = api.pipeline()

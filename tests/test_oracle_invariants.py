@@ -276,3 +276,85 @@ def test_mean_clamp_pin_catches_unclamped_divisor(tmp_path, site):
                           reduction="mean", lib=lib)
     with pytest.raises(AssertionError):
         _check_mean_clamp(r, b)
+
+
+# --- NaN inputs (a reading: the pages do not treat them) ---------------------------------------------
+# A NaN at the blank or a label column of an owned row makes the loss NaN and, under a non-zero weight,
+# every column of the utterance's rows NaN (zero_infinity leaves a NaN loss alone); a NaN at another
+# column shows only in that gradient entry; a zero weight gives zero rows.  Where the NaN lies on a
+# state that some alignment passes through, or outside the label columns, torch's float64 CTC loss and
+# gradient give the same and pin the oracle.  Where no alignment exists, torch's answer depends on the
+# frame of the NaN (NaN or +inf, from the window of states it evaluates); there the reading alone fixes
+# the expected values: loss NaN, rows NaN.
+
+def _nan_cases():
+    rng = np.random.default_rng(77)
+    tg = [1, 1, 2]  # U = 3 with one repeat: at least 4 frames
+    cases = []
+    for label, T, at, zero_inf in [("label column on an alignment", 6, (2, 1), False),
+                                   ("blank column on an alignment", 6, (1, 0), False),
+                                   ("other column", 6, (3, 4), False),
+                                   ("label column on an alignment, zero_infinity", 6, (4, 2), True),
+                                   ("label column, no alignment", 3, (1, 1), False),
+                                   ("label column, no alignment, zero_infinity", 3, (0, 1), True)]:
+        lp = _lp(rng, T, 5, 1.2)
+        lp[at] = np.nan
+        cases.append((label, lp, tg, zero_inf))
+    return cases
+
+
+def _check_nan_case(lib, label, lp, tg, zero_inf):
+    import torch.nn.functional as F
+
+    T = lp.shape[0]
+    r = oracle.ctc_packed(lp, [0, T], [T], np.array([tg], np.int64), [len(tg)], blank=0, zero_infinity=zero_inf,
+                          lib=lib)
+    got_loss = float(r["loss"][0])
+    if "no alignment" in label:
+        assert math.isnan(got_loss) and np.all(np.isnan(r["grad"])), label
+        return
+    x = torch.tensor(lp, dtype=torch.float64)[:, None, :].requires_grad_(True)
+    loss = F.ctc_loss(x, torch.tensor([tg]), [T], [len(tg)], blank=0, reduction="none", zero_infinity=zero_inf)
+    loss.sum().backward()
+    want_loss = float(loss.detach()[0])
+    want_grad = x.grad[:, 0].numpy()
+    assert math.isnan(got_loss) == math.isnan(want_loss), label
+    if not math.isnan(want_loss):
+        np.testing.assert_allclose(got_loss, want_loss, rtol=1e-12, err_msg=label)
+    assert np.array_equal(np.isnan(r["grad"]), np.isnan(want_grad)), label
+    ok = ~np.isnan(want_grad)
+    np.testing.assert_allclose(r["grad"][ok], want_grad[ok], atol=1e-12, err_msg=label)
+
+
+def test_nan_inputs(oracle_mod):
+    for case in _nan_cases():
+        _check_nan_case(None, *case)
+
+
+def test_zero_weight_gives_zero_rows_whatever_the_inputs(oracle_mod):
+    rng = np.random.default_rng(78)
+    lp = _lp(rng, 6, 5, 1.2)
+    lp[2, 4] = np.nan   # a column no state reads
+    lp[3, 1] = np.inf   # and one that exp() turns into inf
+    r = oracle.ctc_packed(lp, [0, 6], [6], np.array([[1, 2]], np.int64), [2], blank=0,
+                          grad_scale=np.zeros(1))
+    assert np.all(r["grad"] == 0.0)
+
+
+def test_nan_pin_catches_a_dropped_nan_rule(tmp_path):
+    # planted mistake: the NaN scan no longer marks the loss; the pins above must reject the oracle
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "ctc_oracle.c")).read()
+    old = "{ n = NAN; break; }"
+    assert old in src
+    mutated = tmp_path / "mut.c"
+    mutated.write_text(src.replace(old, "{ break; }", 1))
+    so = tmp_path / "libmut.so"
+    subprocess.check_call(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", str(mutated), "-o", str(so), "-lm"])
+    lib = oracle.load_library(str(so))
+    failures = 0
+    for case in _nan_cases():
+        try:
+            _check_nan_case(lib, *case)
+        except AssertionError:
+            failures += 1
+    assert failures > 0

@@ -173,6 +173,9 @@ __device__ __forceinline__ void wait_progress(int* prog, int c, int64_t ticks, i
 
 struct Shared {
   unsigned long long ring[kWaves][kR];  // ring[w]: between waves w and w+1; ring[kWaves-1]: sink
+  // per wave, where the lanes other than the edge lane put their (unused) ring stores: every lane
+  // stores each frame, at a distinct address, so the loop needs no change of the execution mask
+  unsigned long long junk[kWaves][64 + kK];
   int prog[kWaves];
   int item;
 };
@@ -189,6 +192,7 @@ struct Ctx {
   unsigned long long* gout;       // global ring written by this block
   unsigned long long* lin;        // LDS ring read by this block
   unsigned long long* lout;       // LDS ring written by this block (a sink if there is no consumer)
+  unsigned long long* junk;       // this wave's junk slots (the ring stores of the other lanes)
   bool lout_live;
   int* prog_cons;
   int* prog_self;
@@ -237,7 +241,8 @@ constexpr int kWaitVm62 = (3 << 14) | (15 << 8) | (7 << 4) | 14;
 // publishes the steps through chunk c-2.  A block ahead of it in the chain has issued its own chunk
 // c-1 and c operations since its chunk c-2 stores, so those have completed as well (at most 63
 // operations can be outstanding).  The last publication, after the last frame, is a device-scope
-// release.  The row side reads the progress word and then performs a device-scope acquire.
+// release.  The row side reads the progress word, then the states and offsets with device-scope
+// loads.
 template <bool BETA, bool IN_GLOBAL, bool OUT_GLOBAL, bool STREAM>
 __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
   const int lane = cx.lane, k = cx.k, T = cx.T, U = cx.U;
@@ -358,10 +363,17 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
           const_cast<float*>(P.E + chunk_lo(c + 1) * Es), 0, static_cast<int>(kK * Es * 4), kRsrcWord3);
       const uint32_t hi = slot_hi(off, c);
       unsigned long long* gslot = cx.gout + row(1 + (int64_t)c * kK);
-      unsigned long long* lslot = cx.lout + ((c * kK) & (kR - 1));
+      // LDS ring: the edge lane's slots of this chunk, the other lanes' junk slots
+      unsigned long long* lslot = lane == edge ? cx.lout + ((c * kK) & (kR - 1)) : cx.junk + lane;
       // the neighbour of frame 0; each later frame's neighbour is formed as soon as the label value
       // it shifts exists, ahead of that frame's stores
       float n = dpp_shifted(lanef(hv, 0), xl, shift);
+      // this lane's byte offset in the chunk's state rows.  In the streamed kernel it is formed anew
+      // each chunk (an empty asm hides its value), so the per-frame offsets beyond the 12-bit
+      // immediate are added in vector registers; kept from chunk to chunk they were held in scalar
+      // registers for the whole loop and reloaded from spill lanes every frame
+      int vo = lane * 8;
+      if (STREAM) __asm__ volatile("" : "+v"(vo));
 #pragma unroll
       for (int i = 0; i < kK; ++i) {
         if (!FULL && i >= nvalid) continue;  // uniform: the last chunk's missing frames
@@ -384,12 +396,16 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
         xl = nl;
         const u32x2 st = BETA ? u32x2{__builtin_bit_cast(uint32_t, pl), __builtin_bit_cast(uint32_t, t)}
                               : u32x2{__builtin_bit_cast(uint32_t, xb), __builtin_bit_cast(uint32_t, xl)};
-        const int so = !ck ? in_chunk(i) * 512 : (((i + 1) & kmask) == 0 ? (((i + 1) >> cx.lk) - 1) * 512 : 0x40000000);
-        __builtin_amdgcn_raw_buffer_store_b64(st, ab, lane * 8, so, STREAM ? kStoreSc1 : 0);
-        if (lane == edge) {
-          const unsigned long long v = pack(xl, hi);
-          if (OUT_GLOBAL) gstore(gslot + drow * i, v);
-          else lstore(lslot + i, v);
+        const int so = !ck ? 0 : (((i + 1) & kmask) == 0 ? (((i + 1) >> cx.lk) - 1) * 512 : 0x40000000);
+        __builtin_amdgcn_raw_buffer_store_b64(st, ab, vo + (!ck ? in_chunk(i) * 512 : 0), so, STREAM ? kStoreSc1 : 0);
+        if (OUT_GLOBAL) {
+          // the lane that passes its label on; the streamed kernel tests it every frame (a mask kept
+          // over the loop took a scalar register pair, reloaded from a spill lane per frame)
+          int ln = lane;
+          if (STREAM) __asm__ volatile("" : "+v"(ln));
+          if (ln == edge) gstore(gslot + drow * i, pack(xl, hi));
+        } else {
+          lstore(lslot + i, pack(xl, hi));
         }
       }
       // each lane shifts by its own integer maximum so that its values stay near 0 (a lane without
@@ -487,6 +503,7 @@ __device__ __forceinline__ void run_wave(const Inputs& in, const Layout& L, cons
   cx.lin = sh.ring[beta ? min(w, kWaves - 2) : max(w - 1, 0)];
   cx.lout_live = has_out && !out_global;
   cx.lout = cx.lout_live ? sh.ring[beta ? w - 1 : w] : sh.ring[kWaves - 1];
+  cx.junk = sh.junk[w];
   cx.prog_cons = &sh.prog[beta ? max(w - 1, 0) : min(w + 1, kWaves - 1)];
   cx.prog_self = &sh.prog[w];
   cx.sig = P.sig + ((dir * Gm + j) * L.NCH + P.cbase[cx.b]) * 64;
@@ -579,26 +596,26 @@ __device__ __forceinline__ void row_band(const Inputs& in, const Layout& L, cons
   const int n1 = re - ra + 1;                                       // frames ra .. re
   const int lo2 = T - 1 - re, hi2 = min(T - 1 - ra, ra - 1);        // and their mirrors
   const int n = n1 + max(hi2 - lo2 + 1, 0);
-  if (w == 0 && !(m.flags & kNoAlignment)) {
+  if (w == 0) {
     wait_steps(P.prog + (2 * b) * kProgStride, re + 1, in.wait_ticks, &P.ctl->err);
     wait_steps(P.prog + (2 * b + 1) * kProgStride, re + 1, in.wait_ticks, &P.ctl->err);
   }
   __syncthreads();  // (also keeps the compiler from moving the row's loads above the wait)
   if (w >= n) return;
   const bool broken = __builtin_amdgcn_readfirstlane(gave_up(&P.ctl->err));
-  const bool nan = m.flags & kNanInput;
-  const bool none = m.flags & kNoAlignment;  // no alignment: its recursions are not run
+  // rows are formed unless the call gave up, the weight is 0, or the utterance has a NaN input or no
+  // alignment (its recursions are not run; the schedule published them as done); a row whose frame
+  // has no mass is filled too
+  const int flags = m.flags;
   const float w0 = utterance_weight(in, L.B, b, false);
+  const bool live = !broken && flags == 0 && w0 != 0.0f;
+  const float fill = !broken && (w0 == 0.0f || (!(flags & kNanInput) && in.zero_infinity)) ? 0.0f : __builtin_nanf("");
   float* acc = reinterpret_cast<float*>(lds);
   for (int i = w; i < n; i += kStreamWaves) {
     const int t = i < n1 ? ra + i : lo2 + (i - n1);
     const int64_t r = (int64_t)m.start + t;
-    if (!broken && !nan && !none && w0 != 0.0f && rows::posterior_stream(L, P, acc, r, b, w0, lane)) {
-      rows::dense_row<DT, true>(in, L, P, grad, lds, r, b, w0, lane, cur_b);
-    } else {
-      const bool zero = !broken && (w0 == 0.0f || (!nan && in.zero_infinity));
-      rows::fill_row<DT>(L, grad, r, zero ? 0.0f : __builtin_nanf(""), lane);
-    }
+    if (live && rows::posterior_stream(L, P, acc, r, b, w0, lane)) rows::dense_row<DT, true>(in, L, P, grad, lds, r, b, w0, lane, cur_b);
+    else rows::fill_row<DT>(L, grad, r, fill, lane);
   }
 }
 

@@ -70,13 +70,16 @@ __global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers
   // No alignment fits when the utterance has fewer frames than its labels need: one frame per label
   // and a blank frame between two equal neighbours (the skip is barred between equal ids).  Such an
   // utterance is marked here; its recursions are not run, since no state path reaches the end.
+  // (U + repeats <= 2U - 1, so only an utterance with fewer frames than that needs the count)
   __shared__ int repeats;
   if (threadIdx.x == 0) repeats = 0;
-  __syncthreads();  // (also: this workgroup's label writes above are visible to its loads below)
-  int rep = 0;
-  for (int j = threadIdx.x + 1; j < mm.U; j += blockDim.x) rep += lab[j + 1] == lab[j];
-  if (rep) atomicAdd(&repeats, rep);
-  __syncthreads();
+  if (mm.U > 0 && mm.T < 2 * mm.U - 1) {  // uniform
+    __syncthreads();  // (also: this workgroup's label writes above are visible to its loads below)
+    int rep = 0;
+    for (int j = threadIdx.x + 1; j < mm.U; j += blockDim.x) rep += lab[j + 1] == lab[j];
+    if (rep) atomicAdd(&repeats, rep);
+    __syncthreads();
+  }
   if (threadIdx.x == 0 && mm.U > 0 && mm.T < mm.U + repeats) {
     // what the recursions' owner blocks would record: an infinite loss and its weight (the gather
     // turns both to those of a NaN loss if it meets a NaN at one of the utterance's columns)
@@ -534,7 +537,8 @@ __device__ void build_bands(const Layout& L, const Pointers& P, const int* sT, c
   __shared__ int bsum[16];
   __shared__ int tmax;
   if (tid == 0) tmax = 0;
-  for (int i = tid; i < 2 * B; i += nt) P.prog[i * kProgStride] = 0;
+  // progress words start at 0; an utterance without alignment has no recursions to wait for
+  for (int i = tid; i < 2 * B; i += nt) P.prog[i * kProgStride] = sU[i >> 1] < 0 ? sT[i >> 1] : 0;
   for (int b = tid; b < B; b += nt) first[b] = bands_of(sT[b]);
   __syncthreads();
   for (int b = tid; b < B; b += nt) atomicMax(&tmax, sT[b]);

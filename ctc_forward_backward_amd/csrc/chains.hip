@@ -362,6 +362,8 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
       const __amdgpu_buffer_rsrc_t er = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float*>(P.E + chunk_lo(c + 1) * Es), 0, static_cast<int>(kK * Es * 4), kRsrcWord3);
       const uint32_t hi = slot_hi(off, c);
+      // the same for the edge lane alone (the global ring's store is made by every lane at once)
+      const uint32_t hi_edge = OUT_GLOBAL ? slot_hi(lanef(off, edge), c) : 0u;
       unsigned long long* gslot = cx.gout + row(1 + (int64_t)c * kK);
       // LDS ring: the edge lane's slots of this chunk, the other lanes' junk slots
       unsigned long long* lslot = lane == edge ? cx.lout + ((c * kK) & (kR - 1)) : cx.junk + lane;
@@ -398,15 +400,11 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
                               : u32x2{__builtin_bit_cast(uint32_t, xb), __builtin_bit_cast(uint32_t, xl)};
         const int so = !ck ? 0 : (((i + 1) & kmask) == 0 ? (((i + 1) >> cx.lk) - 1) * 512 : 0x40000000);
         __builtin_amdgcn_raw_buffer_store_b64(st, ab, vo + (!ck ? in_chunk(i) * 512 : 0), so, STREAM ? kStoreSc1 : 0);
-        if (OUT_GLOBAL) {
-          // the lane that passes its label on; the streamed kernel tests it every frame (a mask kept
-          // over the loop took a scalar register pair, reloaded from a spill lane per frame)
-          int ln = lane;
-          if (STREAM) __asm__ volatile("" : "+v"(ln));
-          if (ln == edge) gstore(gslot + drow * i, pack(xl, hi));
-        } else {
-          lstore(lslot + i, pack(xl, hi));
-        }
+        // the edge lane's label for the next block: to the global ring every lane stores the edge
+        // lane's value (one write to one address), to the LDS ring each lane its own (the other
+        // lanes' go to their junk slots); either way the loop keeps one execution mask
+        if (OUT_GLOBAL) gstore(gslot + drow * i, pack(lanef(xl, edge), hi_edge));
+        else lstore(lslot + i, pack(xl, hi));
       }
       // each lane shifts by its own integer maximum so that its values stay near 0 (a lane without
       // mass keeps its offset)

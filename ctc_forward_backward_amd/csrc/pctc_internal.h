@@ -91,7 +91,8 @@ struct ChainCtl {
   int err;      // non-zero: a wave gave up a bounded wait; the losses of the call are NaN
   int ngroups;
   int nbands;   // streamed pipeline: row bands queued after group 0's recursion segments
-  int pad[5];
+  int arrived;  // streamed pipeline: prep workgroups done (the last one builds the schedule)
+  int pad[4];
   GroupQ g[kMaxGroups];
 };
 
@@ -451,6 +452,10 @@ __device__ __forceinline__ float utterance_weight(const Inputs& in, int64_t B, i
 
 // setup (streamed pipeline): also clears the recursion rings and forms the class maps
 hipError_t launch_prep(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s, bool setup = false);
+// streamed pipeline: the prep launch also builds the schedule (its last workgroup, 256 threads) for
+// batches of up to this many utterances; larger ones take the 1024-thread schedule launch
+constexpr int64_t kScheduleInPrep = 512;
+inline bool schedule_in_prep(const Layout& L) { return L.B <= kScheduleInPrep; }
 // gaps: when given (the gradient), rows owned by no utterance are zeroed in the same launch
 hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s,
                          void* gaps = nullptr);

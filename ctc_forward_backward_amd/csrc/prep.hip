@@ -16,9 +16,10 @@ __global__ void fill_i32_kernel(int* p, int64_t n, int v) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
-// two fills in one launch (the row map, the recursion rings)
-__global__ void fill2_i32_kernel(int* p, int64_t n, int v, int* q, int64_t m, int u) {
+// two fills in one launch (the row map, the recursion rings), and a counter cleared
+__global__ void fill2_i32_kernel(int* p, int64_t n, int v, int* q, int64_t m, int u, int* z) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *z = 0;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < m; i += stride) q[i] = u;
 }
@@ -30,8 +31,12 @@ __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
 // One workgroup per utterance: clamp the metadata so that every later access stays in bounds,
 // write the U+1 distinct class ids of the extended label sequence, claim the utterance's rows.
 __device__ __forceinline__ void class_maps(const Layout& L, const Pointers& P, int b, uint32_t* cw, int* wsum);
+__device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int groups, int bands, int* sh);
 
-__global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers P, int classes) {
+// classes: the class maps too (the streamed pipeline); sched: and the last workgroup to finish builds
+// the streamed pipeline's schedule (one sorted group and the band queue) once every workgroup's
+// metadata is visible
+__global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers P, int classes, int sched) {
   const int b = blockIdx.x;
   __shared__ Meta m;
   if (threadIdx.x == 0) {
@@ -90,9 +95,24 @@ __global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers
     P.w[b] = utterance_weight(in, L.B, b, true);
   }
   if (classes) {  // the class maps of this utterance (its labels were written above, by this workgroup)
-    extern __shared__ uint32_t pcw[];
+    extern __shared__ __attribute__((aligned(16))) uint32_t pcw[];
     __shared__ int wsum[4];
     class_maps(L, P, b, pcw, wsum);
+  }
+  if (sched) {
+    // release this workgroup's writes at device scope, then count it in; the workgroup that counts
+    // last acquires everyone's and schedules (no workgroup waits on another)
+    __shared__ int last;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      last = __hip_atomic_fetch_add(&P.ctl->arrived, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+             static_cast<int>(gridDim.x) - 1;
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    extern __shared__ __attribute__((aligned(16))) int psh[];
+    schedule_body(L, P, 1, 1, 1, psh);
   }
 }
 
@@ -346,10 +366,10 @@ __device__ void block_exclusive_scan(int* a, int n, int* wsum) {
   __syncthreads();
 }
 
-__global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, int sort, int groups, int bands) {
-  // sort ? [T (B) | order (B) | U (B) | rows before each sorted position (B + 1) | queue entries before
-  // each sorted position (B + 1) | bands: first band of each utterance (B + 1)] : unused
-  extern __shared__ int sh[];
+// sh (dynamic LDS): sort ? [T (B) | order (B) | U (B) | rows before each sorted position (B + 1) |
+// queue entries before each sorted position (B + 1) | bands: first band of each utterance (B + 1) |
+// band buckets] : unused
+__device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int groups, int bands, int* sh) {
   __shared__ int wsum[16];
   __shared__ int gfirst[kMaxGroups + 1];
   const int B = static_cast<int>(L.B);
@@ -368,33 +388,50 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
   // 1 + c kChunk .. (c + 1) kChunk, so an utterance of T frames has ceil((T - 1) / kChunk) chunks
   // and, with alpha checkpointing (interval K), the first slot of each utterance's kept steps
   // 0, K, 2K, ... <= T - 1
-  for (int b = tid; b < B; b += nt) {
-    const int T = P.meta[b].T;
-    P.cbase[b] = T > 1 ? (T - 1 + kChunk - 1) / kChunk : 0;
-    P.qbase[b] = T > 0 ? (T - 1) / static_cast<int>(L.K) + 1 : 0;
-  }
-  __syncthreads();
-  block_exclusive_scan(P.cbase, B, wsum);
-  block_exclusive_scan(P.qbase, B, wsum);
+  const int K = static_cast<int>(L.K);
+  auto chunks_of = [](int T) { return T > 1 ? (T - 1 + kChunk - 1) / kChunk : 0; };
+  auto kept_of = [K](int T) { return T > 0 ? (T - 1) / K + 1 : 0; };
+  // a frameless utterance gets its loss here
+  auto frameless = [&](int b, const Meta& m) {
+    if (m.T == 0) {
+      P.nll[b] = m.U == 0 ? 0.0 : (double)INFINITY;
+      P.llb[b] = m.U == 0 ? 0.0 : -(double)INFINITY;
+    }
+  };
   if (sort) {
     int* sT = sh;
     int* order = sh + B;
     int* sU = sh + 2 * B;
     int* cT = sh + 3 * B;
     int* cS = sh + 4 * B + 1;
+    // the metadata, read once; the chunk and kept-step counts are scanned in the space the sorted
+    // sums take afterwards
     for (int b = tid; b < B; b += nt) {
       const Meta m = P.meta[b];
       sT[b] = m.T;
       sU[b] = (m.flags & kNoAlignment) ? -1 : m.U;  // -1: no alignment
+      cT[b] = chunks_of(m.T);
+      cS[b] = kept_of(m.T);
+      frameless(b, m);
     }
     __syncthreads();
+    block_exclusive_scan(cT, B, wsum);
+    block_exclusive_scan(cS, B, wsum);
+    for (int b = tid; b <= B; b += nt) {
+      P.cbase[b] = cT[b];
+      P.qbase[b] = cS[b];
+    }
+    // rank by frame count, longest first (ties by index), four counts per LDS read
     for (int b = tid; b < B; b += nt) {
       const int Tb = sT[b];
-      int rank = 0;
-      for (int c = 0; c < B; ++c) {
-        const int Tc = sT[c];
-        if (Tc > Tb || (Tc == Tb && c < b)) ++rank;
+      int rank = 0, c = 0;
+      const bool vec = (reinterpret_cast<uintptr_t>(sT) & 15) == 0;  // (the dynamic LDS is 16-aligned)
+      for (; vec && c + 4 <= B; c += 4) {
+        const int4 q = *reinterpret_cast<const int4*>(sT + c);
+        rank += (q.x > Tb || (q.x == Tb && c < b)) + (q.y > Tb || (q.y == Tb && c + 1 < b)) +
+                (q.z > Tb || (q.z == Tb && c + 2 < b)) + (q.w > Tb || (q.w == Tb && c + 3 < b));
       }
+      for (; c < B; ++c) rank += sT[c] > Tb || (sT[c] == Tb && c < b);
       order[rank] = b;
     }
     __syncthreads();
@@ -457,6 +494,15 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
       }
     }
   } else {  // too many utterances to sort: identity order, serial (groups is 1 here)
+    for (int b = tid; b < B; b += nt) {
+      const Meta m = P.meta[b];
+      P.cbase[b] = chunks_of(m.T);
+      P.qbase[b] = kept_of(m.T);
+      frameless(b, m);
+    }
+    __syncthreads();
+    block_exclusive_scan(P.cbase, B, wsum);
+    block_exclusive_scan(P.qbase, B, wsum);
     for (int i = tid; i < B; i += nt) P.order[i] = i;
     if (tid == 0) {
       int64_t total = 0;
@@ -499,17 +545,15 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
       P.ctl->ngroups = groups;
     }
   }
-  for (int b = tid; b < B; b += nt) {
-    const Meta m = P.meta[b];
-    if (m.T == 0) {
-      P.nll[b] = m.U == 0 ? 0.0 : (double)INFINITY;
-      P.llb[b] = m.U == 0 ? 0.0 : -(double)INFINITY;
-    }
-  }
   if (bands) {  // streamed pipeline (sorted, one group): the queue of row bands
     __syncthreads();
     build_bands(L, P, sh, sh + 2 * B, sh + 5 * B + 2, sh + 6 * B + 3, kBandBuckets);
   }
+}
+
+__global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, int sort, int groups, int bands) {
+  extern __shared__ __attribute__((aligned(16))) int ssh[];
+  schedule_body(L, P, sort, groups, bands, ssh);
 }
 
 // Streamed pipeline: the queue of row bands (built by the schedule workgroup).  Band k of utterance b
@@ -594,6 +638,12 @@ __device__ void build_bands(const Layout& L, const Pointers& P, const int* sT, c
   }
 }
 
+// dynamic LDS of the schedule: the sorted path's arrays (setup: also the first band per utterance
+// and the band buckets)
+size_t schedule_lds(const Layout& L, bool sort, bool setup) {
+  return sort ? sizeof(int) * (5 * (size_t)L.B + 2 + (setup ? (size_t)L.B + 1 + kBandBuckets + 1 : 0)) : 0;
+}
+
 int grid_for(int64_t n, int threads) {
   int64_t g = (n + threads - 1) / threads;
   if (g > 4096) g = 4096;
@@ -608,15 +658,16 @@ hipError_t launch_prep(const Inputs& in, const Layout& L, const Pointers& P, hip
   const int64_t ring_words = setup ? 2 * 2 * L.Gmax * L.T_total : 0;
   if (L.T_total > 0 || ring_words > 0)
     fill2_i32_kernel<<<grid_for(std::max<int64_t>(L.T_total, ring_words), 256), 256, 0, s>>>(
-        P.rowmap, L.T_total, -1, reinterpret_cast<int*>(P.ring), ring_words, 0);
+        P.rowmap, L.T_total, -1, reinterpret_cast<int*>(P.ring), ring_words, 0, &P.ctl->arrived);
   if (L.B > 0) {
-    const size_t lds = setup ? 2 * sizeof(uint32_t) * (size_t)L.Dw : 0;
+    const bool sched = setup && schedule_in_prep(L);
+    const size_t lds = setup ? std::max(2 * sizeof(uint32_t) * (size_t)L.Dw, sched ? schedule_lds(L, true, true) : 0) : 0;
     if (lds > 48 * 1024) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
       if (e != hipSuccess) return e;
     }
-    prep_kernel<<<static_cast<unsigned>(L.B), 256, lds, s>>>(in, L, P, setup ? 1 : 0);
+    prep_kernel<<<static_cast<unsigned>(L.B), 256, lds, s>>>(in, L, P, setup ? 1 : 0, sched ? 1 : 0);
   }
   return hipGetLastError();
 }
@@ -666,8 +717,7 @@ hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P,
   if (words > 0 && !setup) fill_i32_kernel<<<grid_for(words, 256), 256, 0, s>>>(reinterpret_cast<int*>(P.ring), words, 0);
   const int sort = L.B <= 7168 ? 1 : 0;  // (the sorted path's LDS: 5 B words, at most 140 KB)
   if (setup && !sort) return hipErrorInvalidValue;  // the band queue needs the sorted frame counts
-  // (setup: also the first band per utterance and the band buckets)
-  const size_t lds = sort ? sizeof(int) * (5 * (size_t)L.B + 2 + (setup ? (size_t)L.B + 1 + kBandBuckets + 1 : 0)) : 0;
+  const size_t lds = schedule_lds(L, sort, setup);
   if (lds > 48 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&schedule_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));

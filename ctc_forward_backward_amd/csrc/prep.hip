@@ -332,7 +332,13 @@ __global__ void __launch_bounds__(256) reduce_kernel(const float* losses, const 
 // Frameless utterances get their loss here.
 constexpr int kBandBuckets = 4096;  // LDS buckets of 16 ready steps (a counting sort up to 65535 frames)
 __device__ void build_bands(const Layout& L, const Pointers& P, const int* sT, const int* sU, int* first, int* hist,
-                            int nhist);
+                            int nhist, int* owner, int ocap);
+// LDS words for the band queue's owner map: a bound on the number of bands, at most 8192 (beyond
+// it, each band finds its utterance by a binary search instead)
+__host__ __device__ inline int owner_cap(const Layout& L) {
+  const int64_t n = (L.T_total + L.B) / 32 + 2 * L.B + 1;
+  return static_cast<int>(n < 8192 ? n : 8192);
+}
 
 // exclusive prefix sum of a[0..n) in place, with a[n] = the total (one workgroup; every thread calls
 // it); wsum: blockDim / 64 words of LDS
@@ -369,8 +375,57 @@ __device__ void block_exclusive_scan(int* a, int n, int* wsum) {
 // sh (dynamic LDS): sort ? [T (B) | order (B) | U (B) | rows before each sorted position (B + 1) |
 // queue entries before each sorted position (B + 1) | bands: first band of each utterance (B + 1) |
 // band buckets] : unused
+// the same for two arrays of n at once (one pair of barriers); wsum: 2 blockDim / 64 words
+__device__ void block_exclusive_scan2(int* a, int* c, int n, int* wsum) {
+  const int tid = threadIdx.x, nt = blockDim.x, nw = nt / 64;
+  const int per = (n + nt - 1) / nt;
+  const int i0 = min(tid * per, n), i1 = min(i0 + per, n);
+  int s = 0, u = 0;
+  for (int i = i0; i < i1; ++i) {
+    s += a[i];
+    u += c[i];
+  }
+  const int lane = tid & 63, wave = tid >> 6;
+  int v = s, x = u;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o), y = __shfl_up(x, o);
+    if (lane >= o) {
+      v += t;
+      x += y;
+    }
+  }
+  if (lane == 63) {
+    wsum[wave] = v;
+    wsum[nw + wave] = x;
+  }
+  __syncthreads();
+  int run = v - s, run2 = x - u;
+  for (int k = 0; k < wave; ++k) {
+    run += wsum[k];
+    run2 += wsum[nw + k];
+  }
+  for (int i = i0; i < i1; ++i) {
+    const int p = a[i], q = c[i];
+    a[i] = run;
+    c[i] = run2;
+    run += p;
+    run2 += q;
+  }
+  if (tid == 0) {
+    int t = 0, t2 = 0;
+    for (int k = 0; k < nw; ++k) {
+      t += wsum[k];
+      t2 += wsum[nw + k];
+    }
+    a[n] = t;
+    c[n] = t2;
+  }
+  __syncthreads();
+}
+
 __device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int groups, int bands, int* sh) {
-  __shared__ int wsum[16];
+  __shared__ int wsum[32];
   __shared__ int gfirst[kMaxGroups + 1];
   const int B = static_cast<int>(L.B);
   const int tid = threadIdx.x, nt = blockDim.x;
@@ -415,8 +470,7 @@ __device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int 
       frameless(b, m);
     }
     __syncthreads();
-    block_exclusive_scan(cT, B, wsum);
-    block_exclusive_scan(cS, B, wsum);
+    block_exclusive_scan2(cT, cS, B, wsum);
     for (int b = tid; b <= B; b += nt) {
       P.cbase[b] = cT[b];
       P.qbase[b] = cS[b];
@@ -426,11 +480,16 @@ __device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int 
       const int Tb = sT[b];
       int rank = 0, c = 0;
       const bool vec = (reinterpret_cast<uintptr_t>(sT) & 15) == 0;  // (the dynamic LDS is 16-aligned)
-      for (; vec && c + 4 <= B; c += 4) {
-        const int4 q = *reinterpret_cast<const int4*>(sT + c);
-        rank += (q.x > Tb || (q.x == Tb && c < b)) + (q.y > Tb || (q.y == Tb && c + 1 < b)) +
-                (q.z > Tb || (q.z == Tb && c + 2 < b)) + (q.w > Tb || (q.w == Tb && c + 3 < b));
+      auto before4 = [&](const int4 q, int c0) {
+        return (q.x > Tb || (q.x == Tb && c0 < b)) + (q.y > Tb || (q.y == Tb && c0 + 1 < b)) +
+               (q.z > Tb || (q.z == Tb && c0 + 2 < b)) + (q.w > Tb || (q.w == Tb && c0 + 3 < b));
+      };
+      for (; vec && c + 16 <= B; c += 16) {  // four reads in flight
+        const int4 q0 = *reinterpret_cast<const int4*>(sT + c), q1 = *reinterpret_cast<const int4*>(sT + c + 4);
+        const int4 q2 = *reinterpret_cast<const int4*>(sT + c + 8), q3 = *reinterpret_cast<const int4*>(sT + c + 12);
+        rank += before4(q0, c) + before4(q1, c + 4) + before4(q2, c + 8) + before4(q3, c + 12);
       }
+      for (; vec && c + 4 <= B; c += 4) rank += before4(*reinterpret_cast<const int4*>(sT + c), c);
       for (; c < B; ++c) rank += sT[c] > Tb || (sT[c] == Tb && c < b);
       order[rank] = b;
     }
@@ -442,8 +501,7 @@ __device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int 
       cS[i] = sT[b] > 0 ? 2 * nseg_of(sU[b], sU[b] < 0 ? kNoAlignment : 0) : 0;
     }
     __syncthreads();
-    block_exclusive_scan(cT, B, wsum);
-    block_exclusive_scan(cS, B, wsum);
+    block_exclusive_scan2(cT, cS, B, wsum);
     if (tid == 0) {
       // the cuts: group g takes positions [p0, p1), p1 the first position past p0 where the rows so far
       // reach the group's share, at most B - (groups after it)
@@ -501,8 +559,7 @@ __device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int 
       frameless(b, m);
     }
     __syncthreads();
-    block_exclusive_scan(P.cbase, B, wsum);
-    block_exclusive_scan(P.qbase, B, wsum);
+    block_exclusive_scan2(P.cbase, P.qbase, B, wsum);
     for (int i = tid; i < B; i += nt) P.order[i] = i;
     if (tid == 0) {
       int64_t total = 0;
@@ -547,7 +604,8 @@ __device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int 
   }
   if (bands) {  // streamed pipeline (sorted, one group): the queue of row bands
     __syncthreads();
-    build_bands(L, P, sh, sh + 2 * B, sh + 5 * B + 2, sh + 6 * B + 3, kBandBuckets);
+    build_bands(L, P, sh, sh + 2 * B, sh + 5 * B + 2, sh + 6 * B + 3, kBandBuckets, sh + 6 * B + 4 + kBandBuckets,
+                owner_cap(L));
   }
 }
 
@@ -575,7 +633,7 @@ __device__ __forceinline__ int bands_before(int T, int key) {
 // (one workgroup) sT: the frame counts (LDS, B); sU: the label counts, -1 for an utterance without
 // alignment, whose bands are ready at once and go first; first: B + 1 words of LDS
 __device__ void build_bands(const Layout& L, const Pointers& P, const int* sT, const int* sU, int* first, int* hist,
-                            int nhist) {
+                            int nhist, int* owner, int ocap) {
   const int B = static_cast<int>(L.B);
   const int tid = threadIdx.x, nt = blockDim.x;
   __shared__ int bsum[16];
@@ -589,14 +647,27 @@ __device__ void build_bands(const Layout& L, const Pointers& P, const int* sT, c
   block_exclusive_scan(first, B, bsum);
   const int N = first[B];
   if (tid == 0) P.ctl->nbands = N;
+  // each band's utterance: from an owner map written utterance by utterance (one thread each) when
+  // it fits and the utterances are short (32 bands on average: the serial fill costs less than the
+  // binary searches it replaces), else by a binary search over the first bands
+  const bool map = N <= ocap && N <= 32 * B;
+  if (map) {
+    for (int b = tid; b < B; b += nt)
+      for (int i = first[b]; i < first[b + 1]; ++i) owner[i] = b;
+    __syncthreads();
+  }
   auto band_of = [&](int i, int& b, int& k, int& key) {  // entry i: utterance, band, ready step
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (first[mid] <= i) lo = mid;
-      else hi = mid - 1;
+    if (map) {
+      b = owner[i];
+    } else {
+      int lo = 0, hi = B - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (first[mid] <= i) lo = mid;
+        else hi = mid - 1;
+      }
+      b = lo;
     }
-    b = lo;
     k = i - first[b];
     key = sU[b] < 0 ? 0 : min(sT[b] / 2 + (k + 1) * kBand, sT[b]);
   };
@@ -641,7 +712,8 @@ __device__ void build_bands(const Layout& L, const Pointers& P, const int* sT, c
 // dynamic LDS of the schedule: the sorted path's arrays (setup: also the first band per utterance
 // and the band buckets)
 size_t schedule_lds(const Layout& L, bool sort, bool setup) {
-  return sort ? sizeof(int) * (5 * (size_t)L.B + 2 + (setup ? (size_t)L.B + 1 + kBandBuckets + 1 : 0)) : 0;
+  return sort ? sizeof(int) * (5 * (size_t)L.B + 2 + (setup ? (size_t)L.B + 1 + kBandBuckets + 1 + owner_cap(L) : 0))
+              : 0;
 }
 
 int grid_for(int64_t n, int threads) {

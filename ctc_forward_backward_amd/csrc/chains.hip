@@ -585,7 +585,9 @@ __device__ __forceinline__ void wait_steps(const int* prog, int steps, int64_t t
 // into the wave's LDS, then the gradient row; a row of an utterance with a NaN input, no alignment
 // or a zero weight is filled (NaN, or 0 where the weight is 0 -- under zero_infinity an utterance
 // without alignment has weight 0), and after any give-up the rows are NaN.
-template <int DT>
+// POST (a split forward): the band's rows get their class sums over z in P.post instead (the weights
+// come with the backward, whose gradient rows apply them).
+template <int DT, bool POST>
 __device__ __forceinline__ void row_band(const Inputs& in, const Layout& L, const Pointers& P, void* grad,
                                          uint32_t* lds, int b, int k, int w, int lane, int& cur_b) {
   const Meta m = P.meta[b];
@@ -601,6 +603,19 @@ __device__ __forceinline__ void row_band(const Inputs& in, const Layout& L, cons
   __syncthreads();  // (also keeps the compiler from moving the row's loads above the wait)
   if (w >= n) return;
   const bool broken = __builtin_amdgcn_readfirstlane(gave_up(&P.ctl->err));
+  if (POST) {
+    // every row of an utterance with an alignment and no NaN input (the backward fills the others,
+    // from the loss); a frame without mass gets zero sums
+    if (broken || m.flags != 0) return;
+    float* acc = reinterpret_cast<float*>(lds);
+    for (int i = w; i < n; i += kStreamWaves) {
+      const int64_t r = (int64_t)m.start + (i < n1 ? ra + i : lo2 + (i - n1));
+      const bool ok = rows::posterior_stream(L, P, acc, r, b, 1.0f, lane);
+      float* out = P.post + r * L.C_stride;
+      for (int c = lane; c <= m.U; c += 64) out[c] = ok ? acc[c] : 0.0f;
+    }
+    return;
+  }
   // rows are formed unless the call gave up, the weight is 0, or the utterance has a NaN input or no
   // alignment (its recursions are not run; the schedule published them as done); a row whose frame
   // has no mass is filled too
@@ -622,9 +637,11 @@ __device__ __forceinline__ void row_band(const Inputs& in, const Layout& L, cons
 // 0-3 while the other twelve wait at the barrier; a band runs on all sixteen.  A band is claimed
 // only after every segment has been claimed by a running workgroup, so the recursions it waits for
 // always progress.
-template <int DT>
+// POST: a split forward (see row_band); the backward then skips its posterior pass.
+template <int DT, bool POST>
 __global__ void __launch_bounds__(64 * kStreamWaves, 1) stream_workers(Inputs in, Layout L, Pointers P, void* grad,
                                                                        int per_wave) {
+  if (POST && blockIdx.x == 0 && threadIdx.x == 0) P.ctl->post_ready = 1;
   extern __shared__ __attribute__((aligned(16))) unsigned char ssm[];
   Shared& sh = *reinterpret_cast<Shared*>(ssm);
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -652,8 +669,8 @@ __global__ void __launch_bounds__(64 * kStreamWaves, 1) stream_workers(Inputs in
   int cur_b = -1;
   while (idx < qlen + nbands) {
     const int2 bd = P.bands[idx - qlen];
-    row_band<DT>(in, L, P, grad, lds, __builtin_amdgcn_readfirstlane(bd.x), __builtin_amdgcn_readfirstlane(bd.y), w,
-                 lane, cur_b);
+    row_band<DT, POST>(in, L, P, grad, lds, __builtin_amdgcn_readfirstlane(bd.x), __builtin_amdgcn_readfirstlane(bd.y),
+                       w, lane, cur_b);
     __syncthreads();
     if (tid == 0) sh.item = atomicAdd(&q->qcount, 1);
     __syncthreads();
@@ -713,9 +730,12 @@ hipError_t launch_stream(const Inputs& in, const Layout& L, const Pointers& P, v
     kernel<<<cus > 0 ? cus : 256, 64 * kStreamWaves, lds, s>>>(in, L, P, grad_out, per_wave);
     return hipGetLastError();
   };
-  if (in.dtype == kF32) return launch(&stream_workers<kF32>);
-  if (in.dtype == kF16) return launch(&stream_workers<kF16>);
-  return launch(&stream_workers<kBF16>);
+  // without a gradient (a split forward) the rows' class sums only: no log-prob row is read, so one
+  // kernel serves every dtype
+  if (!grad_out) return launch(&stream_workers<kF32, true>);
+  if (in.dtype == kF32) return launch(&stream_workers<kF32, false>);
+  if (in.dtype == kF16) return launch(&stream_workers<kF16, false>);
+  return launch(&stream_workers<kBF16, false>);
 }
 
 }  // namespace pctc

@@ -130,7 +130,7 @@ __global__ void __launch_bounds__(64 * kCkWaves) ckpt_posterior_kernel(Layout L,
       __syncthreads();
       float ztot = 0.0f;
       for (int i = 0; i < kCkWaves; ++i) ztot += zred[i];  // fixed order
-      const float scale = ztot > 0.0f ? wgt / ztot : 0.0f;
+      const float scale = ztot > 0.0f ? 1.0f / ztot : 0.0f;  // (the gradient rows apply the weight)
       float* out = P.post + r * L.C_stride;
       for (int i = tid; i <= U; i += blockDim.x) {
         out[i] = cacc[i] * scale;

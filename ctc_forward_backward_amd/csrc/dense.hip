@@ -21,6 +21,8 @@ __device__ __forceinline__ int64_t wave_id() {
 }
 
 __global__ void __launch_bounds__(256) posterior_kernel(Layout L, Pointers P, int per_wave, int group) {
+  // a streamed forward has already formed every row's class sums
+  if (__builtin_amdgcn_readfirstlane(P.ctl->post_ready) != 0) return;
   extern __shared__ float psm[];
   const int lane = threadIdx.x & 63;
   float* acc = psm + (threadIdx.x >> 6) * per_wave;
@@ -28,7 +30,7 @@ __global__ void __launch_bounds__(256) posterior_kernel(Layout L, Pointers P, in
   wave_share(P, group, wave_id(), (int64_t)gridDim.x * 4, j0, j1);
   group_rows(P, group, j0, j1, [&](int64_t r, int b) {
     float w;
-    if (rows::row_live(P, b, w)) rows::posterior_row(L, P, acc, r, b, w, lane);
+    if (rows::row_live(P, b, w)) rows::posterior_row(L, P, acc, r, b, lane);
   });
 }
 

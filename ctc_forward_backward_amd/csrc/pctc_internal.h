@@ -92,7 +92,8 @@ struct ChainCtl {
   int ngroups;
   int nbands;   // streamed pipeline: row bands queued after group 0's recursion segments
   int arrived;  // streamed pipeline: prep workgroups done (the last one builds the schedule)
-  int pad[4];
+  int post_ready;  // a streamed forward formed every row's class sums (the backward only forms the rows)
+  int pad[3];
   GroupQ g[kMaxGroups];
 };
 

@@ -535,6 +535,7 @@ __device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int 
       gfirst[groups] = B;
       P.ctl->err = 0;
       P.ctl->ngroups = groups;
+      P.ctl->post_ready = 0;
     }
     __syncthreads();
     for (int i = tid; i < B; i += nt) {
@@ -600,6 +601,7 @@ __device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int 
       }
       P.ctl->err = 0;
       P.ctl->ngroups = groups;
+      P.ctl->post_ready = 0;
     }
   }
   if (bands) {  // streamed pipeline (sorted, one group): the queue of row bands

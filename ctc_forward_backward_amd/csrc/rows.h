@@ -4,10 +4,12 @@
 //
 // Method: NVIDIA-NeMo/Speech pull request "feat(asr): native CTC loss kernel over sequence-packed log
 // probabilities", Triton file, `_beta_grad_kernel` and `_PackedCTCLoss.backward`: the posterior of
-// state s at frame t is exp(alpha + beta - lp + nll) scaled by the utterance's gradient weight and
-// formed only when that weight is non-zero; each gradient row is weight * exp(lp) minus the
-// posteriors summed per class (blank states at the blank column, label states at their label's
-// column); rows owned by no utterance are zero; the row is stored in the dtype of the log probs.
+// state s at frame t is exp(alpha + beta - lp + nll), formed only when the utterance's gradient weight
+// is non-zero; each gradient row is the weight times exp(lp) minus the posteriors summed per class
+// (blank states at the blank column, label states at their label's column); rows owned by no
+// utterance are zero; the row is stored in the dtype of the log probs.  Here the class sums in P.post
+// are kept without the weight (a split forward forms them before the weight is known); the gradient
+// row scales them by it as it loads them.
 //
 // Design for gfx950:
 //   - posterior_row: one pass over the stored alpha and beta (beta is stored without the frame's
@@ -50,7 +52,7 @@ __device__ __forceinline__ bool row_live(const Pointers& P, int b, float& w) {
 
 // class sums of row r of live utterance b (weight w) into P.post; acc: this wave's LDS (C_stride)
 __device__ __forceinline__ void posterior_row(const Layout& L, const Pointers& P, float* acc, int64_t r, int b,
-                                              float w, int lane) {
+                                              int lane) {
   const int64_t TT = L.T_total, Gm = L.Gmax;
   const Meta m = P.meta[b];
   const int U = m.U, G = (U + 64) >> 6;
@@ -113,7 +115,7 @@ __device__ __forceinline__ void posterior_row(const Layout& L, const Pointers& P
   z = wave_sum(z);
   bsum = wave_sum(bsum);
   if (lane == 0) atomicAdd(&acc[dmap[0]], bsum);
-  const float scale = z > 0.0f ? w / z : 0.0f;
+  const float scale = z > 0.0f ? 1.0f / z : 0.0f;
   float* out = P.post + r * L.C_stride;
   for (int i = lane; i <= U; i += 64) out[i] = acc[i] * scale;
 }
@@ -139,8 +141,8 @@ __device__ __forceinline__ float2 ld_dev2(const float* p) {
 // exponent reference is an integer found on the way: the first batch of blocks with mass sets it at
 // its largest term, a later batch with a larger term raises it and scales the sums so far down.  The
 // states and the per-lane offsets are read with device-scope loads (ld_dev).  Leaves the row's class
-// sums times w / z in acc (U+1 floats, by class rank); false when the frame carries no mass (the
-// utterance has no alignment).
+// sums times w / z in acc (U+1 floats, by class rank; w = 1: the sums alone); false when the frame
+// carries no mass (the utterance has no alignment).
 __device__ __forceinline__ bool posterior_stream(const Layout& L, const Pointers& P, float* acc, int64_t r, int b,
                                                  float w, int lane) {
   const int64_t TT = L.T_total, Gm = L.Gmax;
@@ -286,11 +288,11 @@ __device__ __forceinline__ void dense_row(const Inputs& in, const Layout& L, con
   if (!SUMS_IN_LDS) {
 #pragma unroll
     for (int k = 0; k < kPost; ++k)
-      if (lane + 64 * k <= U) acc[lane + 64 * k] = pv[k];
-    for (int i = lane + 64 * kPost; i <= U; i += 64) acc[i] = pr[i];  // long targets
+      if (lane + 64 * k <= U) acc[lane + 64 * k] = pv[k] * w;  // (P.post holds the sums without the weight)
+    for (int i = lane + 64 * kPost; i <= U; i += 64) acc[i] = pr[i] * w;  // long targets
   }
 
-  // stream the row once: w * exp(lp) minus the class posterior at the columns that carry one.
+  // stream the row once: w * exp(lp) minus the class posterior (times w) at the columns that carry one.
   // The classes of an aligned chunk of 8 columns are consecutive in rank order, so one rank per
   // chunk (classes before its first column) locates them all.  Per group of kLook chunks: all
   // bitmap and prefix reads, then the class-sum reads, then the arithmetic, so each kind of

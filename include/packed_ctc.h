@@ -170,8 +170,11 @@ int packed_ctc_loss_noalloc(const void* log_probs, int dtype, int64_t T_total, i
  * `grad_output`).
  *
  * packed_ctc_forward: losses_out and reduced_out exactly as packed_ctc_loss with grad_out = NULL,
- *   and the workspace left holding the recursions' state (alpha, beta, offsets, schedule) that
- *   packed_ctc_backward reads.  Arguments as for packed_ctc_loss.
+ *   and the workspace left holding what packed_ctc_backward reads: with the streamed pipeline
+ *   (float32 / 16-bit inputs, checkpoint_interval 1, up to 2048 utterances) every row's posterior
+ *   sums per class, formed while the recursions run, so the backward only writes the gradient
+ *   rows; otherwise the recursions' state (alpha at every step or every checkpoint_interval-th,
+ *   beta, offsets, schedule).  Arguments as for packed_ctc_loss.
  * packed_ctc_backward: grad_out (T_total, D) exactly as packed_ctc_loss would write it with the
  *   given grad_scale and reduction (w_b = grad_scale[b] or 1, times 1/(B * max(U_b, 1)) for MEAN,
  *   0 under zero_infinity for an infinite loss).  For autograd, grad_scale[b] is the upstream

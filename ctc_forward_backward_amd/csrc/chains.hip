@@ -462,10 +462,27 @@ __device__ __forceinline__ void run_block(const Ctx& cx, const Pointers& P) {
   }
 }
 
-// One block (this wave) of segment `seg` of chain (utterance, direction).
+// The block wave w runs for queue item `item`: one segment of a chain ((chain << 12) | seg: block
+// kWaves seg + w), or both chains of an utterance of at most two blocks (kBothChains | (b << 12):
+// alpha's blocks on waves 0 .. G-1, beta's on waves G .. 2G-1, so each chain's blocks sit on
+// consecutive waves and link through the LDS rings as in a segment).  False: no block for this wave.
+__device__ __forceinline__ bool wave_block(const Pointers& P, int item, int w, int& chain, int& j) {
+  if (item & kBothChains) {
+    const int b = (item & ~kBothChains) >> 12;
+    const int G = (P.meta[b].U + 1 + 63) >> 6;
+    chain = 2 * b + (w >= G ? 1 : 0);
+    j = w >= G ? w - G : w;
+    return w < 2 * G;
+  }
+  chain = item >> 12;
+  j = (item & 4095) * kWaves + w;
+  return true;
+}
+
+// Block j_block of chain (utterance, direction), on wave w of the workgroup.
 template <bool STREAM>
 __device__ __forceinline__ void run_wave(const Inputs& in, const Layout& L, const Pointers& P, Shared& sh, int chain,
-                                         int seg, int w, int lane, bool store) {
+                                         int j_block, int w, int lane, bool store) {
   Ctx cx;
   cx.b = chain >> 1;
   const bool beta = chain & 1;
@@ -474,7 +491,7 @@ __device__ __forceinline__ void run_wave(const Inputs& in, const Layout& L, cons
   cx.U = m.U;
   cx.start = m.start;
   const int G = (cx.U + 1 + 63) >> 6;
-  cx.j = seg * kWaves + w;
+  cx.j = j_block;
   if (cx.j >= G) return;
   const int j = cx.j, U = cx.U;
   cx.lane = lane;
@@ -557,7 +574,8 @@ __global__ void __launch_bounds__(kThreads, 1) chain_workers(Inputs in, Layout L
     const int idx = __builtin_amdgcn_readfirstlane(sh.item);
     if (idx >= qlen) break;
     const int item = __builtin_amdgcn_readfirstlane(items[idx]);
-    run_wave<false>(in, L, P, sh, item >> 12, item & 4095, w, lane, store != 0);
+    int chain, j;
+    if (wave_block(P, item, w, chain, j)) run_wave<false>(in, L, P, sh, chain, j, w, lane, store != 0);
     __syncthreads();
   }
 }
@@ -586,8 +604,8 @@ __device__ __forceinline__ void wait_steps(const int* prog, int steps, int64_t t
 // or a zero weight is filled (NaN, or 0 where the weight is 0 -- under zero_infinity an utterance
 // without alignment has weight 0), and after any give-up the rows are NaN.
 // POST (a split forward): the band's rows get their class sums over z in P.post instead (the weights
-// come with the backward, whose gradient rows apply them).
-template <int DT, bool POST>
+// come with the backward, whose gradient rows apply them).  RB: row chunks per lane in flight.
+template <int DT, bool POST, int RB>
 __device__ __forceinline__ void row_band(const Inputs& in, const Layout& L, const Pointers& P, void* grad,
                                          uint32_t* lds, int b, int k, int w, int lane, int& cur_b) {
   const Meta m = P.meta[b];
@@ -627,7 +645,7 @@ __device__ __forceinline__ void row_band(const Inputs& in, const Layout& L, cons
   for (int i = w; i < n; i += kStreamWaves) {
     const int t = i < n1 ? ra + i : lo2 + (i - n1);
     const int64_t r = (int64_t)m.start + t;
-    if (live && rows::posterior_stream(L, P, acc, r, b, w0, lane)) rows::dense_row<DT, true>(in, L, P, grad, lds, r, b, w0, lane, cur_b);
+    if (live && rows::posterior_stream(L, P, acc, r, b, w0, lane)) rows::dense_row<DT, true, RB>(in, L, P, grad, lds, r, b, w0, lane, cur_b);
     else rows::fill_row<DT>(L, grad, r, fill, lane);
   }
 }
@@ -638,7 +656,7 @@ __device__ __forceinline__ void row_band(const Inputs& in, const Layout& L, cons
 // only after every segment has been claimed by a running workgroup, so the recursions it waits for
 // always progress.
 // POST: a split forward (see row_band); the backward then skips its posterior pass.
-template <int DT, bool POST>
+template <int DT, bool POST, int RB>
 __global__ void __launch_bounds__(64 * kStreamWaves, 1) stream_workers(Inputs in, Layout L, Pointers P, void* grad,
                                                                        int per_wave) {
   if (POST && blockIdx.x == 0 && threadIdx.x == 0) P.ctl->post_ready = 1;
@@ -661,7 +679,8 @@ __global__ void __launch_bounds__(64 * kStreamWaves, 1) stream_workers(Inputs in
     if (idx >= qlen) break;
     if (w < kWaves) {
       const int item = __builtin_amdgcn_readfirstlane(P.items[q->itemoff + idx]);
-      run_wave<true>(in, L, P, sh, item >> 12, item & 4095, w, lane, true);
+      int chain, j;
+      if (wave_block(P, item, w, chain, j)) run_wave<true>(in, L, P, sh, chain, j, w, lane, true);
     }
     __syncthreads();
   }
@@ -669,7 +688,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves, 1) stream_workers(Inputs in
   int cur_b = -1;
   while (idx < qlen + nbands) {
     const int2 bd = P.bands[idx - qlen];
-    row_band<DT, POST>(in, L, P, grad, lds, __builtin_amdgcn_readfirstlane(bd.x), __builtin_amdgcn_readfirstlane(bd.y),
+    row_band<DT, POST, RB>(in, L, P, grad, lds, __builtin_amdgcn_readfirstlane(bd.x), __builtin_amdgcn_readfirstlane(bd.y),
                        w, lane, cur_b);
     __syncthreads();
     if (tid == 0) sh.item = atomicAdd(&q->qcount, 1);
@@ -732,10 +751,13 @@ hipError_t launch_stream(const Inputs& in, const Layout& L, const Pointers& P, v
   };
   // without a gradient (a split forward) the rows' class sums only: no log-prob row is read, so one
   // kernel serves every dtype
-  if (!grad_out) return launch(&stream_workers<kF32, true>);
-  if (in.dtype == kF32) return launch(&stream_workers<kF32, false>);
-  if (in.dtype == kF16) return launch(&stream_workers<kF16, false>);
-  return launch(&stream_workers<kBF16, false>);
+  if (!grad_out) return launch(&stream_workers<kF32, true, 4>);
+  if (in.dtype == kF32) return launch(&stream_workers<kF32, false, 4>);
+  // 16-bit rows of 4096 classes or more: 8 chunks of 16 bytes per lane in flight (half the round trips
+  // of a row; the registers fit beside the recursion's), shorter rows 4 (more would only take registers)
+  const bool wide = L.D >= 4096;
+  if (in.dtype == kF16) return wide ? launch(&stream_workers<kF16, false, 8>) : launch(&stream_workers<kF16, false, 4>);
+  return wide ? launch(&stream_workers<kBF16, false, 8>) : launch(&stream_workers<kBF16, false, 4>);
 }
 
 }  // namespace pctc

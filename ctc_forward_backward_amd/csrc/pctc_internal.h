@@ -102,6 +102,9 @@ struct ChainCtl {
 // [T/2 + k kBand, T/2 + (k+1) kBand): a band can be formed as soon as both recursions have passed
 // its last such step, so the bands of an utterance become ready from the middle frames outwards.
 constexpr int kBand = 16;
+// a queue item holding both chains of one utterance of at most two 64-pair blocks (the recursions'
+// work queue; other items are (chain << 12) | segment)
+constexpr int kBothChains = 1 << 30;
 // Each progress word sits on a cache line of its own (128 bytes): the bands of many utterances poll
 // them from every compute unit while the chains' last blocks write them, and words sharing lines
 // measured up to 55 us slower per call (asr_bpe).

@@ -433,6 +433,12 @@ __device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int 
   auto nseg_of = [](int U, int flags) {
     return (flags & kNoAlignment) ? 0 : (((U + 1 + 63) >> 6) + kSegWaves - 1) / kSegWaves;
   };
+  // queue items of an utterance with frames: one for both chains when each has at most two blocks
+  // (they fill at most the four waves of one workgroup), else one per segment and direction
+  auto items_of = [&](int U, int flags) {
+    if (flags & kNoAlignment) return 0;
+    return ((U + 1 + 63) >> 6) <= 2 ? 1 : 2 * nseg_of(U, flags);
+  };
   // group g ends where the groups so far hold the share of the rows below (each group at least one
   // utterance); its segments in sorted order, each utterance's producers first.  With three
   // groups (cut points measured on uniformly spread lengths): the longest recursions with about
@@ -498,7 +504,7 @@ __device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int 
     for (int i = tid; i < B; i += nt) {
       const int b = order[i];
       cT[i] = sT[b];
-      cS[i] = sT[b] > 0 ? 2 * nseg_of(sU[b], sU[b] < 0 ? kNoAlignment : 0) : 0;
+      cS[i] = sT[b] > 0 ? items_of(sU[b], sU[b] < 0 ? kNoAlignment : 0) : 0;
     }
     __syncthreads();
     block_exclusive_scan2(cT, cS, B, wsum);
@@ -544,9 +550,13 @@ __device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int 
       int g = 0;
       while (g + 1 < groups && gfirst[g + 1] <= i) ++g;
       P.cum[i] = cT[i] - cT[gfirst[g]];
-      if (sT[b] == 0) continue;
-      const int nseg = nseg_of(sU[b], sU[b] < 0 ? kNoAlignment : 0);
+      if (sT[b] == 0 || sU[b] < 0) continue;
       int n = cS[i];
+      if (((sU[b] + 1 + 63) >> 6) <= 2) {
+        P.items[n] = kBothChains | (b << 12);
+        continue;
+      }
+      const int nseg = nseg_of(sU[b], 0);
       for (int j = 0; j < nseg; ++j) {
         P.items[n++] = ((2 * b) << 12) | j;
         P.items[n++] = ((2 * b + 1) << 12) | (nseg - 1 - j);

@@ -37,9 +37,10 @@ constexpr int kBlocks = 4;  // state-pair blocks whose loads are issued together
 constexpr int kLook = 4;    // row chunks whose class lookups are issued together
 constexpr int kPost = 8;    // compact class sums per lane held in registers (U+1 <= 512)
 
-// aligned 8-element row chunks per lane loaded at once.  Four, not a whole row: fewer registers
-// let more waves stream rows side by side, which measured faster than more bytes in flight per
-// wave (a large-vocabulary group: 139 us at 4 chunks, 136 at 8, 153 at 16)
+// aligned 8-element row chunks per lane loaded at once (the default).  Four, not a whole row: fewer
+// registers let more waves stream rows side by side, which measured faster than more bytes in flight
+// per wave (a large-vocabulary group: 139 us at 4 chunks, 136 at 8, 153 at 16).  The streamed
+// kernel takes 8 for 16-bit rows of 4096 classes or more, where its registers allow it.
 template <int DT>
 constexpr int row_batch() { return 4; }
 
@@ -249,7 +250,8 @@ __device__ __forceinline__ void fill_row(const Layout& L, void* grad, int64_t r,
 // wave's words, the class sums (C_stride) then the class bitmap (Dw) and its prefix counts (Dw);
 // cur_b: the utterance whose bitmap the LDS holds (updated here).
 // SUMS_IN_LDS: the class sums are already in the wave's LDS (streamed pipeline), not in P.post.
-template <int DT, bool SUMS_IN_LDS = false>
+// RB: aligned row chunks per lane in flight (row_batch by default)
+template <int DT, bool SUMS_IN_LDS = false, int RB = row_batch<DT>()>
 __device__ __forceinline__ void dense_row(const Inputs& in, const Layout& L, const Pointers& P, void* grad,
                                           uint32_t* lds, int64_t r, int b, float w, int lane, int& cur_b) {
   const int Dw = static_cast<int>(L.Dw);
@@ -257,7 +259,6 @@ __device__ __forceinline__ void dense_row(const Inputs& in, const Layout& L, con
   uint32_t* bits = lds + L.C_stride;
   const int* pref = reinterpret_cast<const int*>(bits + Dw);
   const int64_t D = L.D;
-  constexpr int RB = row_batch<DT>();
   const int64_t f0 = r * D, f1 = f0 + D;
   // aligned chunks [qb, qe) of the row: the first batch and the row's class sums load together
   int64_t a0 = (f0 + 7) & ~int64_t(7), a1 = f1 & ~int64_t(7);

@@ -594,15 +594,15 @@ __device__ __forceinline__ void wait_steps(const int* prog, int steps, int64_t t
   }
 }
 
-// Band k of utterance b (see kBand): one wave waits until both recursions have passed the band (the
-// others wait at the barrier, so polling stays one load per workgroup and microsecond), then the
-// band's rows are shared out over the waves, one row per wave at a time.  The states and offsets the
-// recursions stored on other compute units are read with device-scope loads (rows.h: ld_dev), which
-// take the device-coherent copy; a device-scope acquire here instead (a cache invalidation per band)
-// measured 25-40 us slower per call.  Each row: the posteriors
-// into the wave's LDS, then the gradient row; a row of an utterance with a NaN input, no alignment
-// or a zero weight is filled (NaN, or 0 where the weight is 0 -- under zero_infinity an utterance
-// without alignment has weight 0), and after any give-up the rows are NaN.
+// Band k of utterance b (L.band frames a side, see kBand): one wave waits until both recursions have
+// passed the band (the others wait at the barrier, so polling stays one load per workgroup and
+// microsecond), then the band's rows are shared out over the waves, one row per wave at a time.
+// The states and offsets the recursions stored on other compute units are read with device-scope
+// loads (rows.h: ld_dev), which take the device-coherent copy; a device-scope acquire here instead
+// (a cache invalidation per band) measured 25-40 us slower per call.  Each row: the posteriors into
+// the wave's LDS, then the gradient row; a row of an utterance with a NaN input, no alignment or a
+// zero weight is filled (NaN, or 0 where the weight is 0 -- under zero_infinity an utterance without
+// alignment has weight 0), and after any give-up the rows are NaN.
 // POST (a split forward): the band's rows get their class sums over z in P.post instead (the weights
 // come with the backward, whose gradient rows apply them).  RB: row chunks per lane in flight.
 template <int DT, bool POST, int RB>
@@ -610,7 +610,8 @@ __device__ __forceinline__ void row_band(const Inputs& in, const Layout& L, cons
                                          uint32_t* lds, int b, int k, int w, int lane, int& cur_b) {
   const Meta m = P.meta[b];
   const int T = m.T;
-  const int ra = T / 2 + k * kBand, re = min(ra + kBand, T) - 1;  // its later steps max(t, T-1-t)
+  const int band = band_frames(L, T);
+  const int ra = T / 2 + k * band, re = min(ra + band, T) - 1;  // its later steps max(t, T-1-t)
   const int n1 = re - ra + 1;                                       // frames ra .. re
   const int lo2 = T - 1 - re, hi2 = min(T - 1 - ra, ra - 1);        // and their mirrors
   const int n = n1 + max(hi2 - lo2 + 1, 0);

@@ -62,6 +62,7 @@ struct Layout {
   int64_t C_stride;  // floats per row of the compact class sums (>= Umax + 1)
   int64_t NCH;       // chunk slots of the per-lane offsets: >= sum over utterances of ceil((T - 1) / kChunk)
   int64_t K;         // checkpoint interval of alpha: every K-th step kept (1: every step)
+  int64_t band;      // streamed pipeline: frames a side per row band of a long utterance (by the row's bytes)
   int64_t NQ;        // alpha rows kept per block: T_total (K = 1), else >= sum over utterances of ceil(T / K)
   size_t off_qbase, off_cbase, off_cbits, off_cpref, off_dmap, off_meta, off_lab, off_rowmap, off_rowoff, off_E, off_Eb, off_AB, off_nll, off_llb, off_lsh, off_w, off_post, off_order, off_cum, off_ring,
       off_sig, off_items, off_ctl, off_prog, off_bands, total;
@@ -97,11 +98,22 @@ struct ChainCtl {
   GroupQ g[kMaxGroups];
 };
 
-// Streamed pipeline: the rows of an utterance are handed out in bands of up to 2 kBand rows, band k
-// holding the frames t whose later-finished recursion step max(t, T-1-t) lies in
-// [T/2 + k kBand, T/2 + (k+1) kBand): a band can be formed as soon as both recursions have passed
-// its last such step, so the bands of an utterance become ready from the middle frames outwards.
+// Streamed pipeline: the rows of an utterance are handed out in bands of up to 2 n rows (n = L.band
+// frames a side, kBand or kWideBand), band k holding the frames t whose later-finished recursion step
+// max(t, T-1-t) lies in [T/2 + k n, T/2 + (k+1) n): a band can be formed as soon as both recursions
+// have passed its last such step, so the bands of an utterance become ready from the middle frames
+// outwards.  kBand is also the smallest band, which sizes the band queue.
 constexpr int kBand = 16;
+// bands of kWideBand frames a side where a row (log probs in and gradient out) holds fewer than
+// kBandRowBytes: fewer, larger bands spread each band's fixed cost (its claim, wait and first
+// loads) over more rows, while expensive rows keep the last band of a long utterance short
+constexpr int kWideBand = 24;
+constexpr int64_t kBandRowBytes = 16384;
+// frames a side per band of an utterance with T frames: L.band, or kBand below 4 wide bands (a wide
+// first band of a short utterance would cover most of it and be ready only at its end)
+__host__ __device__ inline int band_frames(const Layout& L, int T) {
+  return T >= 4 * kWideBand ? static_cast<int>(L.band) : kBand;
+}
 // a queue item holding both chains of one utterance of at most two 64-pair blocks (the recursions'
 // work queue; other items are (chain << 12) | segment)
 constexpr int kBothChains = 1 << 30;

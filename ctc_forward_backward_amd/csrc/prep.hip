@@ -627,19 +627,20 @@ __global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, in
 }
 
 // Streamed pipeline: the queue of row bands (built by the schedule workgroup).  Band k of utterance b
-// (T frames) holds the frames whose later recursion step max(t, T-1-t) lies in
-// [T/2 + k kBand, T/2 + (k+1) kBand), and is ready once both recursions have stored
-// min(T/2 + (k+1) kBand, T) steps.  The bands are queued by that step.  Also clears the progress words.
-__device__ __forceinline__ int bands_of(int T) { return T > 0 ? ((T + 1) / 2 + kBand - 1) / kBand : 0; }
+// (T frames; `band` = band_frames(L, T) frames a side) holds the frames whose later recursion step
+// max(t, T-1-t) lies in [T/2 + k band, T/2 + (k+1) band), and is ready once both recursions have
+// stored min(T/2 + (k+1) band, T) steps.  The bands are queued by that step.  Also clears the
+// progress words.
+__device__ __forceinline__ int bands_of(int T, int band) { return T > 0 ? ((T + 1) / 2 + band - 1) / band : 0; }
 
 // bands of an utterance with T frames that become ready before step `key`
-__device__ __forceinline__ int bands_before(int T, int key) {
+__device__ __forceinline__ int bands_before(int T, int key, int band) {
   if (T <= 0) return 0;
-  const int n = bands_of(T);
+  const int n = bands_of(T, band);
   if (key > T) return n;
   const int x = key - T / 2;
   if (x <= 0) return 0;
-  return min(max((x + kBand - 1) / kBand - 1, 0), n);
+  return min(max((x + band - 1) / band - 1, 0), n);
 }
 
 // (one workgroup) sT: the frame counts (LDS, B); sU: the label counts, -1 for an utterance without
@@ -653,7 +654,7 @@ __device__ void build_bands(const Layout& L, const Pointers& P, const int* sT, c
   if (tid == 0) tmax = 0;
   // progress words start at 0; an utterance without alignment has no recursions to wait for
   for (int i = tid; i < 2 * B; i += nt) P.prog[i * kProgStride] = sU[i >> 1] < 0 ? sT[i >> 1] : 0;
-  for (int b = tid; b < B; b += nt) first[b] = bands_of(sT[b]);
+  for (int b = tid; b < B; b += nt) first[b] = bands_of(sT[b], band_frames(L, sT[b]));
   __syncthreads();
   for (int b = tid; b < B; b += nt) atomicMax(&tmax, sT[b]);
   block_exclusive_scan(first, B, bsum);
@@ -681,7 +682,7 @@ __device__ void build_bands(const Layout& L, const Pointers& P, const int* sT, c
       b = lo;
     }
     k = i - first[b];
-    key = sU[b] < 0 ? 0 : min(sT[b] / 2 + (k + 1) * kBand, sT[b]);
+    key = sU[b] < 0 ? 0 : min(sT[b] / 2 + (k + 1) * band_frames(L, sT[b]), sT[b]);
   };
   const int nb = (tmax >> 4) + 1;  // buckets of 16 steps
   if (nb <= nhist) {
@@ -706,7 +707,8 @@ __device__ void build_bands(const Layout& L, const Pointers& P, const int* sT, c
   // longer utterances: the exact order by ready step, ties by utterance (and by band within an
   // utterance without alignment, all of whose bands are ready at step 0), each band's place counted
   auto before = [&](int c, int key) {
-    return sU[c] < 0 ? (key > 0 ? bands_of(sT[c]) : 0) : bands_before(sT[c], key);
+    const int bc = band_frames(L, sT[c]);
+    return sU[c] < 0 ? (key > 0 ? bands_of(sT[c], bc) : 0) : bands_before(sT[c], key, bc);
   };
   for (int i = tid; i < N; i += nt) {
     int b, k, key;

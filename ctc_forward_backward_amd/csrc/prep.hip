@@ -372,9 +372,6 @@ __device__ void block_exclusive_scan(int* a, int n, int* wsum) {
   __syncthreads();
 }
 
-// sh (dynamic LDS): sort ? [T (B) | order (B) | U (B) | rows before each sorted position (B + 1) |
-// queue entries before each sorted position (B + 1) | bands: first band of each utterance (B + 1) |
-// band buckets] : unused
 // the same for two arrays of n at once (one pair of barriers); wsum: 2 blockDim / 64 words
 __device__ void block_exclusive_scan2(int* a, int* c, int n, int* wsum) {
   const int tid = threadIdx.x, nt = blockDim.x, nw = nt / 64;
@@ -424,6 +421,9 @@ __device__ void block_exclusive_scan2(int* a, int* c, int n, int* wsum) {
   __syncthreads();
 }
 
+// sh (dynamic LDS): sort ? [T (B) | order (B) | U (B) | rows before each sorted position (B + 1) |
+// queue entries before each sorted position (B + 1) | bands: first band of each utterance (B + 1) |
+// band buckets] : unused
 __device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int groups, int bands, int* sh) {
   __shared__ int wsum[32];
   __shared__ int gfirst[kMaxGroups + 1];

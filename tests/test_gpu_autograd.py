@@ -360,3 +360,48 @@ def test_float64_autograd_vs_oracle(api, oracle_mod, reduction):
     if reduction != "none":
         np.testing.assert_allclose(float(out.detach().cpu()), ref["reduced"], rtol=1e-10, atol=0)
     assert lp.grad.dtype == torch.float64
+
+
+@pytest.mark.parametrize("pipeline", ["streamed", "grouped"])
+@pytest.mark.parametrize("zero_infinity", [False, True])
+def test_split_edge_cases_vs_oracle(api, oracle_mod, pipeline, zero_infinity):
+    # the split forward leaves the rows of utterances with a NaN input, without an alignment or with a
+    # zero upstream weight to the backward: one frame short of U + repeats and exactly at it,
+    # blank-id labels (blank 6), NaN at a label, at the blank and at a column no state reads
+    _say(f"[gpu autograd] split forward / backward edge cases, {pipeline}, zero_infinity={zero_infinity}")
+    import dataclasses
+
+    cases = [([1, 1, 2], 3), ([1, 1, 2], 4), ([6, 6, 1], 3), ([6, 6, 1], 4), ([2, 4], 9), ([2, 4], 9),
+             ([1, 1, 2], 3), ([5], 7), ([3], 40), ([], 12)]
+    b = W.make_batch([T for _, T in cases], [t for t, _ in cases], 7, seed=41, sigma=1.5, blank=6,
+                     zero_infinity=zero_infinity, reduction="none")
+    lp = b.log_probs.clone()
+    cu = [int(x) for x in b.cu_seqlens]
+    lp[cu[4] + 4, 4] = float("nan")
+    lp[cu[5] + 2, 6] = float("nan")
+    lp[cu[6] + 1, 2] = float("nan")
+    lp[cu[7] + 3, 0] = float("nan")
+    b = dataclasses.replace(b, log_probs=lp)
+    api.set_pipeline(pipeline)
+    try:
+        losses, _, state = api.packed_ctc_forward(lp.to("cuda:0"), *_dev_args(b), blank=6,
+                                                  zero_infinity=zero_infinity, reduction="none")
+        gs = np.linspace(-1.0, 1.0, b.B).astype(np.float32)
+        gs[8] = 0.0
+        grad = api.packed_ctc_backward(state, torch.from_numpy(gs), zero_infinity=zero_infinity, reduction="none")
+        torch.cuda.synchronize()
+    finally:
+        api.set_pipeline("streamed")
+    ref = oracle_mod.ctc_batch(b, reduction="none", grad_scale=gs.astype(np.float64))
+    loss = losses.cpu().double().numpy()
+    assert np.array_equal(np.isnan(loss), np.isnan(ref["loss"]))
+    ok = ~np.isnan(ref["loss"])
+    assert np.array_equal(np.isinf(loss[ok]), np.isinf(ref["loss"][ok]))
+    fin = ok & ~np.isinf(ref["loss"])
+    np.testing.assert_allclose(loss[fin], ref["loss"][fin], rtol=1e-4, atol=1e-5)
+    g = grad.cpu().double().numpy()
+    assert np.array_equal(np.isnan(g), np.isnan(ref["grad"]))
+    m = ~np.isnan(ref["grad"])
+    err = float(np.max(np.abs(g[m] - ref["grad"][m])))
+    _say(f"  max |grad err| = {err:.3e}")
+    assert err <= 1e-4

@@ -29,7 +29,10 @@ namespace pctc {
 namespace {
 
 constexpr int kT64 = 1024;   // threads per workgroup
-constexpr int kPer64 = 16;   // states per thread at most: 16 * 1024 >= 16383 = 2 * 8191 + 1
+// PER, a kernel's template argument: states a thread holds at most (each thread holds ceil or floor
+// of S / n states, n = min(1024, S / 2)): 4 for S <= 4096, 8 for S <= 8192, 16 up to 16383 =
+// 2 * 8191 + 1.  The register arrays take PER entries, so the smallest that fits the call's target
+// bound is launched (16 for every call kept the arrays' registers and spilled them).
 constexpr double kNegInf = -INFINITY;
 
 __device__ __forceinline__ double lse2d(double a, double b) {
@@ -87,6 +90,7 @@ __device__ __forceinline__ bool block_any(bool v, double* red) { return block_su
 // Alpha of utterance blockIdx.x (launched with 1024 threads; threads beyond the split idle at the
 // barriers), the loss, and the NaN flag of the emissions it read.  Workgroup 0 also clears the
 // health word (this path has no waits on other workgroups).
+template <int PER>
 __global__ void __launch_bounds__(kT64) f64_alpha_kernel(Inputs in, Layout L, Pointers P) {
   __shared__ double bnd[2][kT64][2];
   __shared__ double red[32];
@@ -105,12 +109,12 @@ __global__ void __launch_bounds__(kT64) f64_alpha_kernel(Inputs in, Layout L, Po
   const int cnt = active ? sp.hi - sp.lo : 0;
   const int64_t Ss = L.Gmax * 128, D = L.D;
   double* A = reinterpret_cast<double*>(P.ABa);
-  int cls[kPer64];
-  bool skip[kPer64];
-  double a[kPer64];
+  int cls[PER];
+  bool skip[PER];
+  double a[PER];
   bool nan = false;
 #pragma unroll
-  for (int k = 0; k < kPer64; ++k) {
+  for (int k = 0; k < PER; ++k) {
     const int s = sp.lo + k;
     cls[k] = k < cnt ? class_of(lab, s) : 0;
     skip[k] = k < cnt && (s & 1) && s >= 3 && lab[(s + 1) >> 1] != lab[(s - 1) >> 1];
@@ -135,7 +139,7 @@ __global__ void __launch_bounds__(kT64) f64_alpha_kernel(Inputs in, Layout L, Po
       double p1 = tid > 0 ? bnd[buf][tid - 1][0] : kNegInf;
       double p2 = tid > 0 ? bnd[buf][tid - 1][1] : kNegInf;
 #pragma unroll
-      for (int k = 0; k < kPer64; ++k) {
+      for (int k = 0; k < PER; ++k) {
         if (k < cnt) {
           const double cur = a[k];
           double v = lse2d(cur, p1);
@@ -153,7 +157,7 @@ __global__ void __launch_bounds__(kT64) f64_alpha_kernel(Inputs in, Layout L, Po
   // loss: the last blank and the last label at the last frame
   double fin = kNegInf;
 #pragma unroll
-  for (int k = 0; k < kPer64; ++k)
+  for (int k = 0; k < PER; ++k)
     if (k < cnt && sp.lo + k >= S - 2) fin = lse2d(fin, a[k]);
   // the final states sit in at most two threads: combine them as a sum in linear space relative
   // to the larger
@@ -169,6 +173,7 @@ __global__ void __launch_bounds__(kT64) f64_alpha_kernel(Inputs in, Layout L, Po
 
 // Beta of utterance blockIdx.x and, as it passes each frame, the frame's posteriors (from the stored
 // alpha) and its gradient row.  acc: (Umax + 1) doubles of LDS (dynamic), the class sums by rank.
+template <int PER>
 __global__ void __launch_bounds__(kT64) f64_beta_rows_kernel(Inputs in, Layout L, Pointers P, double* grad) {
   extern __shared__ double acc[];
   __shared__ double bnd[2][kT64][2];
@@ -194,11 +199,11 @@ __global__ void __launch_bounds__(kT64) f64_beta_rows_kernel(Inputs in, Layout L
   const bool active = tid < sp.n;
   const int cnt = active ? sp.hi - sp.lo : 0;
   const double* A = reinterpret_cast<const double*>(P.ABa);
-  int cls[kPer64], rank[kPer64];
-  bool skip[kPer64];
-  double bt[kPer64];
+  int cls[PER], rank[PER];
+  bool skip[PER];
+  double bt[PER];
 #pragma unroll
-  for (int k = 0; k < kPer64; ++k) {
+  for (int k = 0; k < PER; ++k) {
     const int s = sp.lo + k;
     cls[k] = k < cnt ? class_of(lab, s) : 0;
     rank[k] = k < cnt ? dmap[(s & 1) ? (s + 1) >> 1 : 0] : 0;
@@ -213,7 +218,7 @@ __global__ void __launch_bounds__(kT64) f64_beta_rows_kernel(Inputs in, Layout L
     // beta at t (emission of frame t included)
     if (t == T - 1) {
 #pragma unroll
-      for (int k = 0; k < kPer64; ++k)
+      for (int k = 0; k < PER; ++k)
         if (k < cnt && sp.lo + k >= S - 2) bt[k] = lp[cls[k]];
     } else {
       const int buf = t & 1;
@@ -228,7 +233,7 @@ __global__ void __launch_bounds__(kT64) f64_beta_rows_kernel(Inputs in, Layout L
         double n1 = last ? kNegInf : bnd[buf][tid + 1][0];
         double n2 = last ? kNegInf : bnd[buf][tid + 1][1];
 #pragma unroll
-        for (int k = kPer64 - 1; k >= 0; --k) {
+        for (int k = PER - 1; k >= 0; --k) {
           if (k < cnt) {
             const double cur = bt[k];
             double v = lse2d(cur, n1);
@@ -241,10 +246,10 @@ __global__ void __launch_bounds__(kT64) f64_beta_rows_kernel(Inputs in, Layout L
       }
     }
     // posteriors of frame t: alpha + beta - lp per state, normalised by the frame's own total
-    double e[kPer64];
+    double e[PER];
     double mx = kNegInf;
 #pragma unroll
-    for (int k = 0; k < kPer64; ++k) {
+    for (int k = 0; k < PER; ++k) {
       e[k] = kNegInf;
       if (k < cnt) {
         const double ak = A[r * Ss + sp.lo + k];
@@ -255,7 +260,7 @@ __global__ void __launch_bounds__(kT64) f64_beta_rows_kernel(Inputs in, Layout L
     mx = block_max(mx, red);
     double z = 0.0;
 #pragma unroll
-    for (int k = 0; k < kPer64; ++k) {
+    for (int k = 0; k < PER; ++k) {
       if (k < cnt && e[k] > kNegInf) {
         e[k] = exp(e[k] - mx);
         z += e[k];
@@ -269,7 +274,7 @@ __global__ void __launch_bounds__(kT64) f64_beta_rows_kernel(Inputs in, Layout L
     // thread first
     double bsum = 0.0;
 #pragma unroll
-    for (int k = 0; k < kPer64; ++k) {
+    for (int k = 0; k < PER; ++k) {
       if (k < cnt && e[k] != 0.0) {
         if ((sp.lo + k) & 1) atomicAdd(&acc[rank[k]], e[k] * scale);
         else bsum += e[k] * scale;
@@ -293,21 +298,37 @@ __global__ void __launch_bounds__(kT64) f64_beta_rows_kernel(Inputs in, Layout L
 
 }  // namespace
 
+// states per thread of the longest target the call allows
+int per_thread(const Layout& L) {
+  const int64_t S = 2 * L.Umax + 1;
+  return S <= 4096 ? 4 : (S <= 8192 ? 8 : 16);
+}
+
 hipError_t launch_f64_alpha(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {
-  f64_alpha_kernel<<<static_cast<unsigned>(L.B > 0 ? L.B : 1), kT64, 0, s>>>(in, L, P);
+  const unsigned grid = static_cast<unsigned>(L.B > 0 ? L.B : 1);
+  const int per = per_thread(L);
+  if (per == 4) f64_alpha_kernel<4><<<grid, kT64, 0, s>>>(in, L, P);
+  else if (per == 8) f64_alpha_kernel<8><<<grid, kT64, 0, s>>>(in, L, P);
+  else f64_alpha_kernel<16><<<grid, kT64, 0, s>>>(in, L, P);
   return hipGetLastError();
 }
 
 hipError_t launch_f64_beta_rows(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s) {
   if (L.B == 0 || L.T_total == 0 || L.D == 0) return hipGetLastError();
   const size_t lds = sizeof(double) * (size_t)(L.Umax + 1);
-  if (lds > 48 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&f64_beta_rows_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-  }
-  f64_beta_rows_kernel<<<static_cast<unsigned>(L.B), kT64, lds, s>>>(in, L, P, static_cast<double*>(grad_out));
-  return hipGetLastError();
+  auto launch = [&](auto kernel) {
+    if (lds > 48 * 1024) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (e != hipSuccess) return e;
+    }
+    kernel<<<static_cast<unsigned>(L.B), kT64, lds, s>>>(in, L, P, static_cast<double*>(grad_out));
+    return hipGetLastError();
+  };
+  const int per = per_thread(L);
+  if (per == 4) return launch(&f64_beta_rows_kernel<4>);
+  if (per == 8) return launch(&f64_beta_rows_kernel<8>);
+  return launch(&f64_beta_rows_kernel<16>);
 }
 
 }  // namespace pctc

@@ -113,7 +113,14 @@ int packed_ctc_max_target_length(const void* target_lengths, int index_flags, in
  *                   (grad_scale ? grad_scale[b] : 1; B values of the loss type, like
  *                   losses_out) times 1/(B * max(U_b, 1)) for MEAN, and 0
  *                   when zero_infinity and nll_b = +inf.  An infeasible utterance with w_b != 0
- *                   gets NaN in every column of its rows.  May be NULL (loss only).
+ *                   gets NaN in every column of its rows; w_b = 0 gives zero rows whatever the
+ *                   log probs hold.  May be NULL (loss only).
+ *   NaN inputs (the page does not treat them): a NaN at the blank's or one of utterance b's label
+ *   columns in any of its rows makes nll_b NaN (zero_infinity leaves a NaN loss alone) and, with
+ *   w_b != 0, every column of its rows NaN; a NaN at any other column shows only in that entry of
+ *   the gradient row.
+ *   An utterance with fewer frames than its labels need (T < U + the number of equal neighbouring
+ *   labels) has no alignment whatever the log probs hold; its recursions are not run.
  *
  * max_target_length >= 0: a caller-promised bound on every target length (no host read; the call
  *   is then graph-capturable).  Lengths beyond it, negative lengths, label ids outside [0, D), or

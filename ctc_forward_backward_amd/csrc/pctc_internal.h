@@ -92,9 +92,8 @@ struct ChainCtl {
   int err;      // non-zero: a wave gave up a bounded wait; the losses of the call are NaN
   int ngroups;
   int nbands;   // streamed pipeline: row bands queued after group 0's recursion segments
-  int arrived;  // streamed pipeline: prep workgroups done (the last one builds the schedule)
   int post_ready;  // a streamed forward formed every row's class sums (the backward only forms the rows)
-  int pad[3];
+  int pad[4];
   GroupQ g[kMaxGroups];
 };
 
@@ -468,13 +467,16 @@ __device__ __forceinline__ float utterance_weight(const Inputs& in, int64_t B, i
 
 // setup (streamed pipeline): also clears the recursion rings and forms the class maps
 hipError_t launch_prep(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s, bool setup = false);
-// streamed pipeline: the prep launch also builds the schedule (its last workgroup, 256 threads) for
-// batches of up to this many utterances; larger ones take the 1024-thread schedule launch
-constexpr int64_t kScheduleInPrep = 512;
-inline bool schedule_in_prep(const Layout& L) { return L.B <= kScheduleInPrep; }
 // gaps: when given (the gradient), rows owned by no utterance are zeroed in the same launch
 hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s,
                          void* gaps = nullptr);
+// streamed pipeline: whether the gather launch also builds the schedule (its first workgroup, beside
+// the gathering ones: the batch has at most 512 utterances and the schedule's LDS fits beside the
+// gather's residency); otherwise the schedule launch runs before the gather
+bool schedule_in_gather(const Layout& L);
+// streamed pipeline: the gather over all rows in their natural order, with the gap rows zeroed when
+// `gaps` is given, and the schedule in its first workgroup when schedule_in_gather(L)
+hipError_t launch_gather_stream(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s, void* gaps);
 // sorts the utterances and cuts them into `groups` groups (see GroupQ)
 // setup (streamed pipeline, one group): the rings are already clear; also builds the row-band queue
 hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P, int groups, hipStream_t s,

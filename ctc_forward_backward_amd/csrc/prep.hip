@@ -16,10 +16,9 @@ __global__ void fill_i32_kernel(int* p, int64_t n, int v) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
-// two fills in one launch (the row map, the recursion rings), and a counter cleared
-__global__ void fill2_i32_kernel(int* p, int64_t n, int v, int* q, int64_t m, int u, int* z) {
+// two fills in one launch (the row map, the recursion rings)
+__global__ void fill2_i32_kernel(int* p, int64_t n, int v, int* q, int64_t m, int u) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *z = 0;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < m; i += stride) q[i] = u;
 }
@@ -31,12 +30,11 @@ __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
 // One workgroup per utterance: clamp the metadata so that every later access stays in bounds,
 // write the U+1 distinct class ids of the extended label sequence, claim the utterance's rows.
 __device__ __forceinline__ void class_maps(const Layout& L, const Pointers& P, int b, uint32_t* cw, int* wsum);
-__device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int groups, int bands, int* sh);
+__device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int groups, int bands, int* sh, int nhist,
+                              int ocap);
 
-// classes: the class maps too (the streamed pipeline); sched: and the last workgroup to finish builds
-// the streamed pipeline's schedule (one sorted group and the band queue) once every workgroup's
-// metadata is visible
-__global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers P, int classes, int sched) {
+// classes: the class maps too (the streamed pipeline)
+__global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers P, int classes) {
   const int b = blockIdx.x;
   __shared__ Meta m;
   if (threadIdx.x == 0) {
@@ -99,21 +97,6 @@ __global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers
     __shared__ int wsum[4];
     class_maps(L, P, b, pcw, wsum);
   }
-  if (sched) {
-    // release this workgroup's writes at device scope, then count it in; the workgroup that counts
-    // last acquires everyone's and schedules (no workgroup waits on another)
-    __shared__ int last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0)
-      last = __hip_atomic_fetch_add(&P.ctl->arrived, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
-             static_cast<int>(gridDim.x) - 1;
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    extern __shared__ __attribute__((aligned(16))) int psh[];
-    schedule_body(L, P, 1, 1, 1, psh);
-  }
 }
 
 // One wave per owned row: the log2 emissions of the row at the utterance's U+1 label columns,
@@ -132,76 +115,115 @@ __device__ __forceinline__ float ld1(const void* p, int64_t i) {
   else return __builtin_bit_cast(float, static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
 }
 
+// The label ids of the utterance a wave is on (kept while its rows follow one another)
+struct GatherCur {
+  int b = -1, U = 0;
+  const int* lab = nullptr;
+  int col[kGLab];
+};
+
+template <int DT>
+__device__ __forceinline__ void gather_row(const Inputs& in, const Layout& L, const Pointers& P, int64_t r, int b,
+                                           GatherCur& g, int lane) {
+  if (b != g.b) {
+    g.U = P.meta[b].U;
+    g.lab = P.lab + (int64_t)b * (L.Umax + 1);
+#pragma unroll
+    for (int k = 0; k < kGLab; ++k) g.col[k] = g.lab[min(lane + 64 * k, g.U)];
+    g.b = b;
+  }
+  const int U = g.U;
+  float* E = P.E + r * L.E_stride;
+  const int64_t row = r * L.D;
+  float mx = kNeg;
+  int nan = 0;
+  if (U < 64 * kGLab) {
+    float v[kGLab];
+#pragma unroll
+    for (int k = 0; k < kGLab; ++k) v[k] = ld1<DT>(in.log_probs, row + g.col[k]);  // all loads in flight
+#pragma unroll
+    for (int k = 0; k < kGLab; ++k) {
+      const bool ok = lane + 64 * k <= U;
+      float x = v[k] * kLog2e;
+      nan |= ok && (x != x);
+      x = fmaxf(x, kNeg);  // -inf (and NaN, flagged above) become the finite sentinel
+      v[k] = x;
+      if (ok) mx = fmaxf(mx, x);
+    }
+    mx = wave_max(mx);
+    const float off = mx > kNegHalf ? floorf(mx) : 0.0f;
+#pragma unroll
+    for (int k = 0; k < kGLab; ++k)
+      if (lane + 64 * k <= U) E[lane + 64 * k] = v[k] - off;
+    if (lane == 0) P.rowoff[r] = static_cast<int>(off);
+  } else {  // long targets: two passes over the table row
+    for (int j = lane; j <= U; j += 64) {
+      float x = ld1<DT>(in.log_probs, row + g.lab[j]) * kLog2e;
+      nan |= (x != x);
+      x = fmaxf(x, kNeg);
+      mx = fmaxf(mx, x);
+      E[j] = x;
+    }
+    mx = wave_max(mx);
+    const float off = mx > kNegHalf ? floorf(mx) : 0.0f;
+    for (int j = lane; j <= U; j += 64) E[j] -= off;
+    if (lane == 0) P.rowoff[r] = static_cast<int>(off);
+  }
+  if (lane == 0) {
+    E[U + 1] = kNeg;  // the column of label states that do not exist
+    P.Eb[r] = E[0];   // (this lane wrote E[0] above)
+  }
+  if (nan) {
+    atomicOr(&P.meta[b].flags, kNanInput);
+    if (P.meta[b].flags & kNoAlignment) {  // its loss is NaN, not +inf (no recursion will say so)
+      P.nll[b] = (double)NAN;
+      P.w[b] = utterance_weight(in, L.B, b, false);
+    }
+  }
+}
+
 template <int DT>
 __global__ void __launch_bounds__(256) gather_kernel(Inputs in, Layout L, Pointers P, int group, void* gaps) {
   const int lane = threadIdx.x & 63;
   const int64_t wid = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int64_t j0, j1;
   wave_share(P, group, wid, (int64_t)gridDim.x * 4, j0, j1);
-  const int64_t D = L.D;
-  int cur_b = -1, U = 0;
-  const int* lab = nullptr;
-  int col[kGLab];
-  group_rows(P, group, j0, j1, [&](int64_t r, int b) {
-    if (b != cur_b) {
-      U = P.meta[b].U;
-      lab = P.lab + (int64_t)b * (L.Umax + 1);
-#pragma unroll
-      for (int k = 0; k < kGLab; ++k) col[k] = lab[min(lane + 64 * k, U)];
-      cur_b = b;
-    }
-    float* E = P.E + r * L.E_stride;
-    const int64_t row = r * D;
-    float mx = kNeg;
-    int nan = 0;
-    if (U < 64 * kGLab) {
-      float v[kGLab];
-#pragma unroll
-      for (int k = 0; k < kGLab; ++k) v[k] = ld1<DT>(in.log_probs, row + col[k]);  // all loads in flight
-#pragma unroll
-      for (int k = 0; k < kGLab; ++k) {
-        const bool ok = lane + 64 * k <= U;
-        float x = v[k] * kLog2e;
-        nan |= ok && (x != x);
-        x = fmaxf(x, kNeg);  // -inf (and NaN, flagged above) become the finite sentinel
-        v[k] = x;
-        if (ok) mx = fmaxf(mx, x);
-      }
-      mx = wave_max(mx);
-      const float off = mx > kNegHalf ? floorf(mx) : 0.0f;
-#pragma unroll
-      for (int k = 0; k < kGLab; ++k)
-        if (lane + 64 * k <= U) E[lane + 64 * k] = v[k] - off;
-      if (lane == 0) P.rowoff[r] = static_cast<int>(off);
-    } else {  // long targets: two passes over the table row
-      for (int j = lane; j <= U; j += 64) {
-        float x = ld1<DT>(in.log_probs, row + lab[j]) * kLog2e;
-        nan |= (x != x);
-        x = fmaxf(x, kNeg);
-        mx = fmaxf(mx, x);
-        E[j] = x;
-      }
-      mx = wave_max(mx);
-      const float off = mx > kNegHalf ? floorf(mx) : 0.0f;
-      for (int j = lane; j <= U; j += 64) E[j] -= off;
-      if (lane == 0) P.rowoff[r] = static_cast<int>(off);
-    }
-    if (lane == 0) {
-      E[U + 1] = kNeg;  // the column of label states that do not exist
-      P.Eb[r] = E[0];   // (this lane wrote E[0] above)
-    }
-    if (nan) {
-      atomicOr(&P.meta[b].flags, kNanInput);
-      if (P.meta[b].flags & kNoAlignment) {  // its loss is NaN, not +inf (no recursion will say so)
-        P.nll[b] = (double)NAN;
-        P.w[b] = utterance_weight(in, L.B, b, false);
-      }
-    }
-  });
-  if (gaps) {  // streamed pipeline: rows owned by no utterance get a zero gradient here
+  GatherCur g;
+  group_rows(P, group, j0, j1, [&](int64_t r, int b) { gather_row<DT>(in, L, P, r, b, g, lane); });
+  if (gaps) {  // rows owned by no utterance get a zero gradient here
     const int64_t waves = (int64_t)gridDim.x * 4;
     for (int64_t r = wid; r < L.T_total; r += waves)
       if (__builtin_amdgcn_readfirstlane(P.rowmap[r]) < 0) rows::fill_row<DT>(L, gaps, r, 0.0f, lane);
+  }
+}
+
+// Streamed pipeline (one group): the rows in their natural order, each wave a contiguous share, its
+// rows' owners read in one load; rows owned by no utterance get a zero gradient when `gaps` is given.
+// With sched (nhist, ocap: see schedule_body), workgroup 0 builds the schedule instead, beside the
+// gathering workgroups: it reads only what prep wrote, and nothing here reads what it writes.
+template <int DT>
+__global__ void __launch_bounds__(256) gather_stream_kernel(Inputs in, Layout L, Pointers P, void* gaps, int sched,
+                                                            int nhist, int ocap) {
+  if (sched && blockIdx.x == 0) {
+    extern __shared__ __attribute__((aligned(16))) int gsh[];
+    schedule_body(L, P, 1, 1, 1, gsh, nhist, ocap);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int64_t first = sched ? 1 : 0;
+  const int64_t waves = ((int64_t)gridDim.x - first) * 4;
+  const int64_t wid = ((int64_t)blockIdx.x - first) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t per = (L.T_total + waves - 1) / waves;
+  const int64_t r0 = min(wid * per, L.T_total), r1 = min(r0 + per, L.T_total);
+  GatherCur g;
+  for (int64_t q = r0; q < r1; q += 64) {
+    const int n = static_cast<int>(min((int64_t)64, r1 - q));
+    const int own = lane < n ? P.rowmap[q + lane] : -1;
+    for (int i = 0; i < n; ++i) {
+      const int b = __builtin_amdgcn_readlane(own, i);
+      if (b >= 0) gather_row<DT>(in, L, P, q + i, b, g, lane);
+      else if (gaps) rows::fill_row<DT>(L, gaps, q + i, 0.0f, lane);
+    }
   }
 }
 
@@ -424,7 +446,9 @@ __device__ void block_exclusive_scan2(int* a, int* c, int n, int* wsum) {
 // sh (dynamic LDS): sort ? [T (B) | order (B) | U (B) | rows before each sorted position (B + 1) |
 // queue entries before each sorted position (B + 1) | bands: first band of each utterance (B + 1) |
 // band buckets] : unused
-__device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int groups, int bands, int* sh) {
+// bands: nhist band buckets and an owner map of up to ocap bands in sh (see schedule_lds)
+__device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int groups, int bands, int* sh, int nhist,
+                              int ocap) {
   __shared__ int wsum[32];
   __shared__ int gfirst[kMaxGroups + 1];
   const int B = static_cast<int>(L.B);
@@ -616,14 +640,14 @@ __device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int 
   }
   if (bands) {  // streamed pipeline (sorted, one group): the queue of row bands
     __syncthreads();
-    build_bands(L, P, sh, sh + 2 * B, sh + 5 * B + 2, sh + 6 * B + 3, kBandBuckets, sh + 6 * B + 4 + kBandBuckets,
-                owner_cap(L));
+    build_bands(L, P, sh, sh + 2 * B, sh + 5 * B + 2, sh + 6 * B + 3, nhist, sh + 6 * B + 4 + nhist, ocap);
   }
 }
 
-__global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, int sort, int groups, int bands) {
+__global__ void __launch_bounds__(1024) schedule_kernel(Layout L, Pointers P, int sort, int groups, int bands,
+                                                        int nhist, int ocap) {
   extern __shared__ __attribute__((aligned(16))) int ssh[];
-  schedule_body(L, P, sort, groups, bands, ssh);
+  schedule_body(L, P, sort, groups, bands, ssh, nhist, ocap);
 }
 
 // Streamed pipeline: the queue of row bands (built by the schedule workgroup).  Band k of utterance b
@@ -723,11 +747,32 @@ __device__ void build_bands(const Layout& L, const Pointers& P, const int* sT, c
   }
 }
 
-// dynamic LDS of the schedule: the sorted path's arrays (setup: also the first band per utterance
-// and the band buckets)
-size_t schedule_lds(const Layout& L, bool sort, bool setup) {
-  return sort ? sizeof(int) * (5 * (size_t)L.B + 2 + (setup ? (size_t)L.B + 1 + kBandBuckets + 1 + owner_cap(L) : 0))
-              : 0;
+// dynamic LDS of the schedule: the sorted path's arrays (setup: also the first band per utterance,
+// nhist + 1 band buckets and an owner map of ocap words)
+size_t schedule_lds(const Layout& L, bool sort, bool setup, int nhist, int ocap) {
+  return sort ? sizeof(int) * (5 * (size_t)L.B + 2 + (setup ? (size_t)L.B + 1 + nhist + 1 + ocap : 0)) : 0;
+}
+
+// The schedule in the gather launch: at most 512 utterances, and LDS that leaves the gather's
+// residency (7 workgroups of 4 waves per compute unit, set by its registers) as it is: buckets for
+// ready steps up to the batch's frame count (at most kBandBuckets), and an owner map as far as the
+// rest allows (beyond it, the bands find their utterance by binary search)
+constexpr size_t kGatherSchedLds = 22 * 1024;
+struct GatherSched {
+  bool on = false;
+  int nhist = 0, ocap = 0;
+  size_t lds = 0;
+};
+GatherSched gather_sched(const Layout& L) {
+  GatherSched g;
+  if (L.B < 1 || L.B > 512) return g;
+  g.nhist = static_cast<int>(std::min<int64_t>(kBandBuckets, L.T_total / 16 + 2));
+  const size_t base = schedule_lds(L, true, true, g.nhist, 0);
+  if (base > kGatherSchedLds) return g;
+  g.ocap = static_cast<int>(std::min<int64_t>(owner_cap(L), (int64_t)((kGatherSchedLds - base) / sizeof(int))));
+  g.lds = std::max(kRowKernelLds, schedule_lds(L, true, true, g.nhist, g.ocap));
+  g.on = true;
+  return g;
 }
 
 int grid_for(int64_t n, int threads) {
@@ -744,16 +789,15 @@ hipError_t launch_prep(const Inputs& in, const Layout& L, const Pointers& P, hip
   const int64_t ring_words = setup ? 2 * 2 * L.Gmax * L.T_total : 0;
   if (L.T_total > 0 || ring_words > 0)
     fill2_i32_kernel<<<grid_for(std::max<int64_t>(L.T_total, ring_words), 256), 256, 0, s>>>(
-        P.rowmap, L.T_total, -1, reinterpret_cast<int*>(P.ring), ring_words, 0, &P.ctl->arrived);
+        P.rowmap, L.T_total, -1, reinterpret_cast<int*>(P.ring), ring_words, 0);
   if (L.B > 0) {
-    const bool sched = setup && schedule_in_prep(L);
-    const size_t lds = setup ? std::max(2 * sizeof(uint32_t) * (size_t)L.Dw, sched ? schedule_lds(L, true, true) : 0) : 0;
+    const size_t lds = setup ? 2 * sizeof(uint32_t) * (size_t)L.Dw : 0;
     if (lds > 48 * 1024) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
       if (e != hipSuccess) return e;
     }
-    prep_kernel<<<static_cast<unsigned>(L.B), 256, lds, s>>>(in, L, P, setup ? 1 : 0, sched ? 1 : 0);
+    prep_kernel<<<static_cast<unsigned>(L.B), 256, lds, s>>>(in, L, P, setup ? 1 : 0);
   }
   return hipGetLastError();
 }
@@ -775,6 +819,34 @@ hipError_t launch_gather(const Inputs& in, const Layout& L, const Pointers& P, i
   else if (in.dtype == kF16) gather_kernel<kF16><<<grid, 256, lds, s>>>(in, L, P, group, gaps);
   else gather_kernel<kBF16><<<grid, 256, lds, s>>>(in, L, P, group, gaps);
   return hipGetLastError();
+}
+
+bool schedule_in_gather(const Layout& L) { return gather_sched(L).on; }
+
+hipError_t launch_gather_stream(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s, void* gaps) {
+  const GatherSched gs = gather_sched(L);
+  if (L.T_total == 0 && !gs.on) return hipGetLastError();
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  // as in the grouped gather: 16 workgroups per compute unit, each wave a contiguous share of the
+  // rows (plus the schedule's workgroup)
+  const int grid = 16 * (cus > 0 ? cus : 256) + (gs.on ? 1 : 0);
+  const size_t lds = gs.on ? gs.lds : kRowKernelLds;
+  auto go = [&](auto kern) {
+    if (lds > 48 * 1024) {
+      hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      if (e2 != hipSuccess) return e2;
+    }
+    kern<<<grid, 256, lds, s>>>(in, L, P, gaps, gs.on ? 1 : 0, gs.nhist, gs.ocap);
+    return hipGetLastError();
+  };
+  if (in.dtype == kF32) return go(&gather_stream_kernel<kF32>);
+  if (in.dtype == kF64) return go(&gather_stream_kernel<kF64>);
+  if (in.dtype == kF16) return go(&gather_stream_kernel<kF16>);
+  return go(&gather_stream_kernel<kBF16>);
 }
 
 hipError_t launch_classes(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {
@@ -803,13 +875,14 @@ hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P,
   if (words > 0 && !setup) fill_i32_kernel<<<grid_for(words, 256), 256, 0, s>>>(reinterpret_cast<int*>(P.ring), words, 0);
   const int sort = L.B <= 7168 ? 1 : 0;  // (the sorted path's LDS: 5 B words, at most 140 KB)
   if (setup && !sort) return hipErrorInvalidValue;  // the band queue needs the sorted frame counts
-  const size_t lds = schedule_lds(L, sort, setup);
+  const int nhist = kBandBuckets, ocap = owner_cap(L);
+  const size_t lds = schedule_lds(L, sort, setup, nhist, ocap);
   if (lds > 48 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&schedule_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  schedule_kernel<<<1, 1024, lds, s>>>(L, P, sort, groups, setup ? 1 : 0);
+  schedule_kernel<<<1, 1024, lds, s>>>(L, P, sort, groups, setup ? 1 : 0, nhist, ocap);
   return hipGetLastError();
 }
 

@@ -58,7 +58,7 @@ __global__ void __launch_bounds__(256) gap_kernel(Layout L, Pointers P, void* gr
   const int lane = threadIdx.x & 63;
   const int64_t r0 = wave_id() * rows_per_wave, r1 = min(r0 + rows_per_wave, L.T_total);
   for (int64_t r = r0; r < r1; ++r)
-    if (__builtin_amdgcn_readfirstlane(P.rowmap[r]) < 0) rows::fill_row<DT>(L, grad, r, 0.0f, lane);
+    if (__builtin_amdgcn_readfirstlane(row_owner(L, P, r)) < 0) rows::fill_row<DT>(L, grad, r, 0.0f, lane);
 }
 
 int compute_units() {

@@ -130,7 +130,7 @@ constexpr int kMaxCheckpointBlocks = 16;  // checkpointed utterances: up to 16 s
 struct Pointers {
   Meta* meta;
   int* lab;      // (B, Umax + 1): j = 0 the blank, j >= 1 targets[b][j-1]
-  int* rowmap;   // (T_total,): owning utterance or -1
+  int* rowmap;   // (T_total,): owning utterance, written for owned rows only (see row_owner)
   int* rowoff;   // (T_total,): integer offset subtracted from the row's gathered log2 emissions
   float* E;      // (T_total, E_stride): columns 0..U the labels, U+1 holds -1e30; kEPad rows of padding on either side
   float* Eb;     // (T_total,): column 0 of E (the blank) again, contiguous for the recursions; kEPad padding each side
@@ -234,6 +234,16 @@ __device__ __forceinline__ void group_rows(const Pointers& P, int g, int64_t j0,
     for (int64_t k = 0; k < take; ++k) fn(m.start + off + k, b);
     if (take > 0) j += take;
   }
+}
+
+// The utterance that owns row r, or -1.  The row map is written for owned rows only; the entry of a
+// row that no utterance owns is left from earlier use of the workspace and names (if any) an
+// utterance whose rows do not hold r, so an entry counts only where that utterance's rows hold r.
+__device__ __forceinline__ int row_owner(const Layout& L, const Pointers& P, int64_t r) {
+  const int b = P.rowmap[r];
+  if (b < 0 || b >= L.B) return -1;
+  const Meta m = P.meta[b];
+  return r >= m.start && r < (int64_t)m.start + m.T ? b : -1;
 }
 
 // list entries [j0, j1) of wave `wid` out of `waves` over group g's rows

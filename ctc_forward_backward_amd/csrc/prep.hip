@@ -16,13 +16,6 @@ __global__ void fill_i32_kernel(int* p, int64_t n, int v) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
 }
 
-// two fills in one launch (the row map, the recursion rings)
-__global__ void fill2_i32_kernel(int* p, int64_t n, int v, int* q, int64_t m, int u) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < m; i += stride) q[i] = u;
-}
-
 __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0u;
 }
@@ -33,8 +26,16 @@ __device__ __forceinline__ void class_maps(const Layout& L, const Pointers& P, i
 __device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int groups, int bands, int* sh, int nhist,
                               int ocap);
 
-// classes: the class maps too (the streamed pipeline)
-__global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers P, int classes) {
+// classes: the class maps too (the streamed pipeline).  Workgroups past the B utterances' (streamed
+// pipeline) clear the recursion rings' ring_words words instead: every slot starts unwritten (its
+// written mark clear), and nothing else in this launch touches them.
+__global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers P, int classes, int64_t ring_words) {
+  if (blockIdx.x >= L.B) {
+    const int64_t fills = gridDim.x - L.B;
+    int* q = reinterpret_cast<int*>(P.ring);
+    for (int64_t i = (blockIdx.x - L.B) * 256 + threadIdx.x; i < ring_words; i += fills * 256) q[i] = 0;
+    return;
+  }
   const int b = blockIdx.x;
   __shared__ Meta m;
   if (threadIdx.x == 0) {
@@ -193,12 +194,13 @@ __global__ void __launch_bounds__(256) gather_kernel(Inputs in, Layout L, Pointe
   if (gaps) {  // rows owned by no utterance get a zero gradient here
     const int64_t waves = (int64_t)gridDim.x * 4;
     for (int64_t r = wid; r < L.T_total; r += waves)
-      if (__builtin_amdgcn_readfirstlane(P.rowmap[r]) < 0) rows::fill_row<DT>(L, gaps, r, 0.0f, lane);
+      if (__builtin_amdgcn_readfirstlane(row_owner(L, P, r)) < 0) rows::fill_row<DT>(L, gaps, r, 0.0f, lane);
   }
 }
 
 // Streamed pipeline (one group): the rows in their natural order, each wave a contiguous share, its
-// rows' owners read in one load; rows owned by no utterance get a zero gradient when `gaps` is given.
+// rows' owners found 64 at a time (as row_owner does); rows owned by no utterance get a zero gradient
+// when `gaps` is given.
 // With sched (nhist, ocap: see schedule_body), workgroup 0 builds the schedule instead, beside the
 // gathering workgroups: it reads only what prep wrote, and nothing here reads what it writes.
 template <int DT>
@@ -218,7 +220,13 @@ __global__ void __launch_bounds__(256) gather_stream_kernel(Inputs in, Layout L,
   GatherCur g;
   for (int64_t q = r0; q < r1; q += 64) {
     const int n = static_cast<int>(min((int64_t)64, r1 - q));
-    const int own = lane < n ? P.rowmap[q + lane] : -1;
+    int own = lane < n ? P.rowmap[q + lane] : -1;
+    if (own < 0 || own >= L.B) {
+      own = -1;
+    } else {
+      const Meta m = P.meta[own];
+      if (q + lane < m.start || q + lane >= (int64_t)m.start + m.T) own = -1;
+    }
     for (int i = 0; i < n; ++i) {
       const int b = __builtin_amdgcn_readlane(own, i);
       if (b >= 0) gather_row<DT>(in, L, P, q + i, b, g, lane);
@@ -784,12 +792,10 @@ int grid_for(int64_t n, int threads) {
 }  // namespace
 
 hipError_t launch_prep(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s, bool setup) {
-  // setup (streamed pipeline): the recursion rings are cleared here too (one fill launch) and the class
-  // maps are formed by the prep workgroups
+  // setup (streamed pipeline): the recursion rings are cleared by workgroups of the same launch and
+  // the class maps are formed by the prep workgroups.  The row map is written for owned rows only
+  // (row_owner tells the others).
   const int64_t ring_words = setup ? 2 * 2 * L.Gmax * L.T_total : 0;
-  if (L.T_total > 0 || ring_words > 0)
-    fill2_i32_kernel<<<grid_for(std::max<int64_t>(L.T_total, ring_words), 256), 256, 0, s>>>(
-        P.rowmap, L.T_total, -1, reinterpret_cast<int*>(P.ring), ring_words, 0);
   if (L.B > 0) {
     const size_t lds = setup ? 2 * sizeof(uint32_t) * (size_t)L.Dw : 0;
     if (lds > 48 * 1024) {
@@ -797,7 +803,8 @@ hipError_t launch_prep(const Inputs& in, const Layout& L, const Pointers& P, hip
                                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
       if (e != hipSuccess) return e;
     }
-    prep_kernel<<<static_cast<unsigned>(L.B), 256, lds, s>>>(in, L, P, setup ? 1 : 0);
+    const int fills = ring_words > 0 ? std::min(grid_for(ring_words, 256), 1024) : 0;
+    prep_kernel<<<static_cast<unsigned>(L.B + fills), 256, lds, s>>>(in, L, P, setup ? 1 : 0, ring_words);
   }
   return hipGetLastError();
 }

@@ -107,6 +107,7 @@ __global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers
 // a contiguous range of rows: the label ids of its utterance stay in registers from row to row,
 // and for U+1 <= 512 the values too, so the table row is written once.
 constexpr int kGLab = 8;  // label columns per lane held in registers
+static_assert(4 * 64 * kGLab * sizeof(float) <= kRowKernelLds, "the streamed gather's class-ordered rows use 64 kGLab floats of LDS per wave");
 
 template <int DT>
 __device__ __forceinline__ float ld1(const void* p, int64_t i) {
@@ -116,12 +117,104 @@ __device__ __forceinline__ float ld1(const void* p, int64_t i) {
   else return __builtin_bit_cast(float, static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
 }
 
-// The label ids of the utterance a wave is on (kept while its rows follow one another)
+// the same, non-temporal (the line is not kept in the caches)
+template <int DT>
+__device__ __forceinline__ float ld1_nt(const void* p, int64_t i) {
+  if constexpr (DT == kF32) return __builtin_nontemporal_load(static_cast<const float*>(p) + i);
+  else if constexpr (DT == kF64) return static_cast<float>(__builtin_nontemporal_load(static_cast<const double*>(p) + i));
+  else if constexpr (DT == kF16) return static_cast<float>(__builtin_nontemporal_load(static_cast<const _Float16*>(p) + i));
+  else
+    return __builtin_bit_cast(float, static_cast<uint32_t>(__builtin_nontemporal_load(static_cast<const uint16_t*>(p) + i))
+                                         << 16);
+}
+
+// The label ids of the utterance a wave is on (kept while its rows follow one another); in the
+// class-ordered form (gather_row_sorted), the utterance's classes in increasing order and the rank
+// of each label's class instead
 struct GatherCur {
-  int b = -1, U = 0;
+  int b = -1, U = 0, ncls = 0;
   const int* lab = nullptr;
   int col[kGLab];
+  int dm[kGLab];
 };
+
+// Streamed pipeline, U + 1 <= 64 kGLab: the row's values at the utterance's distinct classes, read
+// in increasing column order (lane i of load k takes the class of rank 64 k + i), so that each
+// 128-byte line is requested by one load, and with non-temporal loads: the log probs are read again
+// only by the gradient rows, much later, and their lines kept in the caches would displace the
+// emission table written here, which the recursions read next (large_vocab: the stream launch
+// 16 us faster; with the values read in label order, where one line serves several loads, the
+// non-temporal form fetched lines again and the gather took 30 us longer).  The values go to the
+// label order through the wave's LDS (wl: 64 kGLab floats).  Uses the class maps (class_maps).
+template <int DT>
+__device__ __forceinline__ void gather_row_sorted(const Inputs& in, const Layout& L, const Pointers& P, int64_t r,
+                                                  int b, GatherCur& g, int lane, float* wl) {
+  if (b != g.b) {
+    // the classes by rank: the bitmap's set bits in order, written at their ranks
+    const int Dw = static_cast<int>(L.Dw);
+    const uint32_t* gb = P.cbits + (int64_t)b * Dw;
+    const int* gp = P.cpref + (int64_t)b * Dw;
+    g.U = P.meta[b].U;
+    g.ncls = gp[Dw - 1] + __builtin_popcount(gb[Dw - 1]);
+    for (int i = lane; i < Dw; i += 64) {
+      uint32_t bits = gb[i];
+      int k = gp[i];
+      while (bits) {
+        const int e = __builtin_ctz(bits);
+        bits &= bits - 1u;
+        wl[k++] = static_cast<float>(32 * i + e);  // (exact: class ids are below 2^24)
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int* dmap = P.dmap + (int64_t)b * (L.Umax + 1);
+#pragma unroll
+    for (int k = 0; k < kGLab; ++k) {
+      g.col[k] = static_cast<int>(wl[min(lane + 64 * k, g.ncls - 1)]);
+      g.dm[k] = dmap[min(lane + 64 * k, g.U)];
+    }
+    g.b = b;
+  }
+  const int U = g.U, n = g.ncls;
+  float* E = P.E + r * L.E_stride;
+  const int64_t row = r * L.D;
+  float v[kGLab];
+#pragma unroll
+  for (int k = 0; k < kGLab; ++k) v[k] = ld1_nt<DT>(in.log_probs, row + g.col[k]);  // all loads in flight
+  float mx = kNeg;
+  int nan = 0;
+#pragma unroll
+  for (int k = 0; k < kGLab; ++k) {
+    const bool ok = lane + 64 * k < n;
+    float x = v[k] * kLog2e;
+    nan |= ok && (x != x);
+    x = fmaxf(x, kNeg);  // -inf (and NaN, flagged above) become the finite sentinel
+    v[k] = x;
+    if (ok) mx = fmaxf(mx, x);
+  }
+  mx = wave_max(mx);
+  const float off = mx > kNegHalf ? floorf(mx) : 0.0f;
+  // LDS operations of one wave complete in order: these writes follow the reads of the previous
+  // row (or of the class list) and precede the reads below
+#pragma unroll
+  for (int k = 0; k < kGLab; ++k)
+    if (lane + 64 * k < n) wl[lane + 64 * k] = v[k] - off;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int k = 0; k < kGLab; ++k)
+    if (lane + 64 * k <= U) E[lane + 64 * k] = wl[g.dm[k]];
+  if (lane == 0) {
+    P.rowoff[r] = static_cast<int>(off);
+    E[U + 1] = kNeg;          // the column of label states that do not exist
+    P.Eb[r] = wl[g.dm[0]];    // the blank's value (label 0)
+  }
+  if (nan) {
+    atomicOr(&P.meta[b].flags, kNanInput);
+    if (P.meta[b].flags & kNoAlignment) {  // its loss is NaN, not +inf (no recursion will say so)
+      P.nll[b] = (double)NAN;
+      P.w[b] = utterance_weight(in, L.B, b, false);
+    }
+  }
+}
 
 template <int DT>
 __device__ __forceinline__ void gather_row(const Inputs& in, const Layout& L, const Pointers& P, int64_t r, int b,
@@ -203,11 +296,15 @@ __global__ void __launch_bounds__(256) gather_kernel(Inputs in, Layout L, Pointe
 // when `gaps` is given.
 // With sched (nhist, ocap: see schedule_body), workgroup 0 builds the schedule instead, beside the
 // gathering workgroups: it reads only what prep wrote, and nothing here reads what it writes.
-template <int DT>
+// SORTED: rows of up to 64 kGLab labels are read in class order (gather_row_sorted); taken for rows
+// of at least kSortedRowBytes, where it pays (on short rows the lines serve every load anyway, and
+// its registers cost occupancy: small and char_level 8 us slower)
+constexpr int64_t kSortedRowBytes = 4096;
+template <int DT, bool SORTED>
 __global__ void __launch_bounds__(256) gather_stream_kernel(Inputs in, Layout L, Pointers P, void* gaps, int sched,
                                                             int nhist, int ocap) {
+  extern __shared__ __attribute__((aligned(16))) int gsh[];  // (at least 4 waves x 64 kGLab words)
   if (sched && blockIdx.x == 0) {
-    extern __shared__ __attribute__((aligned(16))) int gsh[];
     schedule_body(L, P, 1, 1, 1, gsh, nhist, ocap);
     return;
   }
@@ -217,7 +314,8 @@ __global__ void __launch_bounds__(256) gather_stream_kernel(Inputs in, Layout L,
   const int64_t wid = ((int64_t)blockIdx.x - first) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t per = (L.T_total + waves - 1) / waves;
   const int64_t r0 = min(wid * per, L.T_total), r1 = min(r0 + per, L.T_total);
-  GatherCur g;
+  GatherCur g, gc;  // label-ordered and class-ordered rows
+  float* wl = reinterpret_cast<float*>(gsh) + (threadIdx.x >> 6) * (64 * kGLab);
   for (int64_t q = r0; q < r1; q += 64) {
     const int n = static_cast<int>(min((int64_t)64, r1 - q));
     int own = lane < n ? P.rowmap[q + lane] : -1;
@@ -229,8 +327,12 @@ __global__ void __launch_bounds__(256) gather_stream_kernel(Inputs in, Layout L,
     }
     for (int i = 0; i < n; ++i) {
       const int b = __builtin_amdgcn_readlane(own, i);
-      if (b >= 0) gather_row<DT>(in, L, P, q + i, b, g, lane);
-      else if (gaps) rows::fill_row<DT>(L, gaps, q + i, 0.0f, lane);
+      if (b >= 0) {
+        if (SORTED && P.meta[b].U < 64 * kGLab) gather_row_sorted<DT>(in, L, P, q + i, b, gc, lane, wl);
+        else gather_row<DT>(in, L, P, q + i, b, g, lane);  // (wave-uniform)
+      } else if (gaps) {
+        rows::fill_row<DT>(L, gaps, q + i, 0.0f, lane);
+      }
     }
   }
 }
@@ -850,10 +952,11 @@ hipError_t launch_gather_stream(const Inputs& in, const Layout& L, const Pointer
     kern<<<grid, 256, lds, s>>>(in, L, P, gaps, gs.on ? 1 : 0, gs.nhist, gs.ocap);
     return hipGetLastError();
   };
-  if (in.dtype == kF32) return go(&gather_stream_kernel<kF32>);
-  if (in.dtype == kF64) return go(&gather_stream_kernel<kF64>);
-  if (in.dtype == kF16) return go(&gather_stream_kernel<kF16>);
-  return go(&gather_stream_kernel<kBF16>);
+  const bool sorted = L.D * (in.dtype == kF32 ? 4 : 2) >= kSortedRowBytes;
+  if (in.dtype == kF32) return sorted ? go(&gather_stream_kernel<kF32, true>) : go(&gather_stream_kernel<kF32, false>);
+  if (in.dtype == kF64) return go(&gather_stream_kernel<kF64, false>);
+  if (in.dtype == kF16) return sorted ? go(&gather_stream_kernel<kF16, true>) : go(&gather_stream_kernel<kF16, false>);
+  return sorted ? go(&gather_stream_kernel<kBF16, true>) : go(&gather_stream_kernel<kBF16, false>);
 }
 
 hipError_t launch_classes(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {

@@ -316,6 +316,22 @@ def test_large_vocabulary_lds_accumulator(api, oracle_mod):
     compare(run_gpu(api, b), oracle_mod.ctc_batch(b), torch.bfloat16, "D=30000")
 
 
+@pytest.mark.parametrize("dtype,D", [("f16", 4096), ("f32", 1024)])
+def test_wide_rows_class_and_label_order(api, oracle_mod, dtype, D):
+    # rows of 4 KB or more: the streamed gather reads utterances of up to 512 labels in class order
+    # and longer ones in label order; both kinds, a label-free utterance and an unowned row between
+    # utterances, next to each other so that waves pass from one kind to the other
+    _say(f"[gpu parity] wide rows, both gather orders ({dtype}, D = {D})")
+    rng = np.random.default_rng(21)
+    lengths = [1500, 640, 7, 900]
+    tl = [700, 300, 0, 511]
+    targets = [[int(x) for x in rng.integers(1, D, size=u)] for u in tl]
+    b = W.make_batch(lengths, targets, D, seed=21, sigma=3.0, dtype=dtype, reduction="sum", gaps=[0, 0, 1, 0])
+    ref = oracle_mod.ctc_batch(b)
+    got = run_gpu(api, b)
+    compare(got, ref, torch.float16 if dtype == "f16" else torch.float32, f"wide rows {dtype}")
+
+
 def test_loss_only_and_explicit_bound(api, oracle_mod):
     b = W.small()
     ref = oracle_mod.ctc_batch(b, want_grad=False)

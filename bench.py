@@ -181,12 +181,21 @@ def extras(api, dev, stream):
     args = tuple(x.to(dev) for x in (b.cu_seqlens, b.lengths, b.targets, b.target_lengths))
     kw = dict(blank=b.blank, reduction=b.reduction, max_target_length=int(b.target_lengths.max()))
 
+    half = torch.tensor(0.5, device=dev)
+
     def fwd_bwd():
         lp.grad = None
         api.ctc_loss(lp, *args, **kw).backward()
 
-    out["autograd_large_vocab"] = {"ms_forward_backward": _median_ms(stream, fwd_bwd, 10),
-                                   "note": "ctc_loss(...).backward(): packed_ctc_forward + packed_ctc_backward"}
+    def fwd_bwd_scaled():
+        lp.grad = None
+        api.ctc_loss(lp, *args, **kw).backward(half)
+
+    out["autograd_large_vocab"] = {
+        "ms_forward_backward": _median_ms(stream, fwd_bwd, 10),
+        "ms_forward_backward_upstream_0.5": _median_ms(stream, fwd_bwd_scaled, 10),
+        "note": "ctc_loss(...).backward(): packed_ctc_forward_grad writes the rows for a unit upstream gradient, "
+                "packed_ctc_backward_update keeps them (upstream 1) or rewrites them (upstream 0.5)"}
     del lp
     rng = np.random.default_rng(31)
     lengths = [int(x) for x in rng.integers(1, 400, size=11)] + [0, 3]

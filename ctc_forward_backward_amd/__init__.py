@@ -4,8 +4,9 @@
 loaded lazily so that the input generators in ``workloads`` import without the HIP library.
 """
 
-_API = ("packed_ctc_loss", "packed_ctc_forward", "packed_ctc_backward", "ctc_loss", "PackedCTCLoss", "packed_ctc_reduce",
-        "packed_ctc_workspace_size", "PackedCTCError", "library_path", "hmm_forward")
+_API = ("packed_ctc_loss", "packed_ctc_forward", "packed_ctc_backward", "packed_ctc_forward_grad",
+        "packed_ctc_backward_update", "ctc_loss", "PackedCTCLoss", "packed_ctc_reduce", "packed_ctc_workspace_size",
+        "PackedCTCError", "library_path", "hmm_forward")
 
 
 def __getattr__(name):

@@ -26,6 +26,7 @@ namespace {
 constexpr int kCkWaves = kMaxCheckpointBlocks;
 
 __global__ void __launch_bounds__(64 * kCkWaves) ckpt_posterior_kernel(Layout L, Pointers P) {
+  if (skipped(P)) return;
   extern __shared__ float cacc[];  // C_stride floats: the current row's class sums by rank
   __shared__ float edge_v[2][kCkWaves];
   __shared__ int edge_o[2][kCkWaves];

@@ -22,7 +22,7 @@ __device__ __forceinline__ int64_t wave_id() {
 
 __global__ void __launch_bounds__(256) posterior_kernel(Layout L, Pointers P, int per_wave, int group) {
   // a streamed forward has already formed every row's class sums
-  if (__builtin_amdgcn_readfirstlane(P.ctl->post_ready) != 0) return;
+  if (__builtin_amdgcn_readfirstlane(P.ctl->post_ready) != 0 || skipped(P)) return;
   extern __shared__ float psm[];
   const int lane = threadIdx.x & 63;
   float* acc = psm + (threadIdx.x >> 6) * per_wave;
@@ -37,6 +37,7 @@ __global__ void __launch_bounds__(256) posterior_kernel(Layout L, Pointers P, in
 template <int DT>
 __global__ void __launch_bounds__(256) dense_kernel(Inputs in, Layout L, Pointers P, void* grad, int per_wave,
                                                     int group) {
+  if (skipped(P)) return;
   extern __shared__ uint32_t dsm[];
   const int lane = threadIdx.x & 63;
   uint32_t* lds = dsm + (threadIdx.x >> 6) * per_wave;
@@ -55,6 +56,7 @@ __global__ void __launch_bounds__(256) dense_kernel(Inputs in, Layout L, Pointer
 // rows owned by no utterance (gaps between utterances, over-allocation) get a zero gradient
 template <int DT>
 __global__ void __launch_bounds__(256) gap_kernel(Layout L, Pointers P, void* grad, int rows_per_wave) {
+  if (skipped(P)) return;
   const int lane = threadIdx.x & 63;
   const int64_t r0 = wave_id() * rows_per_wave, r1 = min(r0 + rows_per_wave, L.T_total);
   for (int64_t r = r0; r < r1; ++r)

@@ -175,6 +175,7 @@ __global__ void __launch_bounds__(kT64) f64_alpha_kernel(Inputs in, Layout L, Po
 // alpha) and its gradient row.  acc: (Umax + 1) doubles of LDS (dynamic), the class sums by rank.
 template <int PER>
 __global__ void __launch_bounds__(kT64) f64_beta_rows_kernel(Inputs in, Layout L, Pointers P, double* grad) {
+  if (skipped(P)) return;
   extern __shared__ double acc[];
   __shared__ double bnd[2][kT64][2];
   __shared__ double red[32];

@@ -93,7 +93,10 @@ struct ChainCtl {
   int ngroups;
   int nbands;   // streamed pipeline: row bands queued after group 0's recursion segments
   int post_ready;  // a streamed forward formed every row's class sums (the backward only forms the rows)
-  int pad[4];
+  int rows_for;    // 1 + zero_infinity + 2 reduction: the gradient rows for unit upstream weights were
+                   // written by the forward with these (packed_ctc_forward_grad); 0 otherwise
+  int unit;        // a gradient update found unit upstream weights for rows_for: its row kernels skip
+  int pad[2];
   GroupQ g[kMaxGroups];
 };
 
@@ -167,7 +170,14 @@ struct Pointers {
   // first
   int* prog;        // (2 B) words, kProgStride ints apart
   int2* bands;      // (T_total / kBand + 2 B + 1): at most ceil(ceil(T/2) / kBand) <= T/64 + 2 per utterance
+  // the gradient update (packed_ctc_backward_update): &ctl->unit, which its row kernels read first
+  // and return at once when set; null in every other call
+  const int* skip;
 };
+// a row kernel of a gradient update whose rows the forward already wrote
+__device__ __forceinline__ bool skipped(const Pointers& P) {
+  return P.skip && __builtin_amdgcn_readfirstlane(*P.skip) != 0;
+}
 
 Pointers carve(void* workspace, const Layout& L);
 
@@ -499,8 +509,11 @@ constexpr int64_t kHmmMaxTable = 16384;  // S * O floats of the emission table i
 
 // store: keep alpha, beta and the block offsets for the posteriors (false: the loss only)
 hipError_t launch_chains(const Inputs& in, const Layout& L, const Pointers& P, int group, bool store, hipStream_t s);
+// rows: 0, or kRowsMark (the call wrote the gradient for unit upstream weights: recorded in
+// ctl->rows_for), or kRowsUpdate (a gradient update: sets ctl->unit, see ChainCtl)
+constexpr int kRowsMark = 1, kRowsUpdate = 2;
 hipError_t launch_weights(const Inputs& in, const Layout& L, const Pointers& P, void* losses_out, void* reduced_out,
-                          hipStream_t s);
+                          hipStream_t s, int rows = 0);
 hipError_t launch_classes(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
 hipError_t launch_posteriors(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s);
 hipError_t launch_dense(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, int group, hipStream_t s);

@@ -388,6 +388,7 @@ __device__ __forceinline__ void class_maps(const Layout& L, const Pointers& P, i
 }
 
 __global__ void __launch_bounds__(256) classes_kernel(Layout L, Pointers P) {
+  if (skipped(P)) return;
   extern __shared__ uint32_t cw[];  // Dw bitmap words, then Dw prefix counts
   __shared__ int wsum[4];
   class_maps(L, P, blockIdx.x, cw, wsum);
@@ -396,8 +397,11 @@ __global__ void __launch_bounds__(256) classes_kernel(Layout L, Pointers P) {
 // Losses after zero_infinity, gradient weights and the sum / mean reduction (one workgroup,
 // a fixed summation tree so that the reduced value is reproducible).
 __global__ void __launch_bounds__(256) weights_kernel(Inputs in, Layout L, Pointers P, void* losses_out,
-                                                      void* reduced_out) {
+                                                      void* reduced_out, int rows) {
   __shared__ double part[256];
+  __shared__ int nonunit;
+  if (threadIdx.x == 0) nonunit = 0;
+  __syncthreads();
   double acc = 0.0;
   const int64_t B = L.B;
   // a wave of the recursions gave up a bounded wait: the results of the call are unspecified, and
@@ -415,6 +419,7 @@ __global__ void __launch_bounds__(256) weights_kernel(Inputs in, Layout L, Point
     int64_t U = load_index(in.target_lengths, in.index_flags & 8, b);
     const double Uc = U > 1 ? (double)U : 1.0;
     double w = grad_scale_of(in, b);
+    if (rows == kRowsUpdate && w != 1.0) nonunit = 1;
     if (in.reduction == 2) w /= (double)B * Uc;
     if (in.zero_infinity && inf) w = 0.0;
     P.w[b] = static_cast<float>(w);
@@ -425,6 +430,19 @@ __global__ void __launch_bounds__(256) weights_kernel(Inputs in, Layout L, Point
   for (int h = 128; h > 0; h >>= 1) {
     if (threadIdx.x < h) part[threadIdx.x] += part[threadIdx.x + h];
     __syncthreads();
+  }
+  // the record of what grad_out holds: rows for unit upstream weights (a forward that wrote them), or
+  // not (any other call; an update with other weights rewrites the rows); an update with unit
+  // weights and the forward's zero_infinity and reduction leaves them as they are
+  if (threadIdx.x == 0) {
+    const int mark = 1 + in.zero_infinity + 2 * in.reduction;
+    if (rows == kRowsUpdate) {
+      const bool unit = !nonunit && P.ctl->rows_for == mark;
+      P.ctl->unit = unit ? 1 : 0;
+      if (!unit) P.ctl->rows_for = 0;
+    } else {
+      P.ctl->rows_for = rows == kRowsMark ? mark : 0;
+    }
   }
   if (threadIdx.x == 0 && reduced_out && in.reduction != 0) {
     double v = part[0];
@@ -997,8 +1015,8 @@ hipError_t launch_schedule(const Inputs& in, const Layout& L, const Pointers& P,
 }
 
 hipError_t launch_weights(const Inputs& in, const Layout& L, const Pointers& P, void* losses_out, void* reduced_out,
-                          hipStream_t s) {
-  weights_kernel<<<1, 256, 0, s>>>(in, L, P, losses_out, reduced_out);
+                          hipStream_t s, int rows) {
+  weights_kernel<<<1, 256, 0, s>>>(in, L, P, losses_out, reduced_out, rows);
   return hipGetLastError();
 }
 

@@ -209,6 +209,39 @@ int packed_ctc_backward(const void* log_probs, int dtype, int64_t T_total, int64
                         int checkpoint_interval, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The split for autograd when the upstream gradient is usually one (a reduced loss that is
+ * backpropagated as it is): the forward writes the gradient too, and the backward leaves it alone
+ * when the upstream weights are all one, deciding on the device (no host read, graph-capturable).
+ * [PR] `_PackedCTCLoss.backward` forms the rows with `grad_output` as each utterance's weight; these
+ * calls give the same rows.
+ *
+ * packed_ctc_forward_grad: losses_out, reduced_out and grad_out exactly as packed_ctc_loss with
+ *   grad_scale = NULL (w_b from the reduction and zero_infinity alone), and the workspace left
+ *   holding what packed_ctc_backward reads, with a record that grad_out holds the rows for unit
+ *   upstream weights under this zero_infinity and reduction.  max_target_length must be >= 0
+ *   (PCTC_ERR_ARG otherwise).  Other arguments as for packed_ctc_loss.
+ * packed_ctc_backward_update: grad_out as packed_ctc_backward writes it, with one difference: when
+ *   every grad_scale[b] is exactly 1 (or grad_scale is NULL) and zero_infinity and reduction are
+ *   the forward's, the rows are left as they are and no row is read or written (a few microseconds).
+ *   Precondition, beside packed_ctc_backward's: grad_out is the buffer packed_ctc_forward_grad
+ *   wrote, changed since only by packed_ctc_backward_update calls on the same workspace (an update
+ *   with other weights rewrites the rows and clears the record, so a later update with unit
+ *   weights rewrites them again).  Arguments, error codes and alignment as for packed_ctc_backward.
+ * Both calls are asynchronous on `stream` and allocate nothing.
+ */
+int packed_ctc_forward_grad(const void* log_probs, int dtype, int64_t T_total, int64_t D, const void* cu_seqlens,
+                            const void* lengths, int64_t B, const void* targets, int64_t target_width,
+                            const void* target_lengths, int index_flags, int64_t max_target_length, int blank,
+                            int zero_infinity, int reduction, void* losses_out, void* reduced_out, void* grad_out,
+                            int checkpoint_interval, void* workspace, size_t workspace_bytes, void* stream);
+
+int packed_ctc_backward_update(const void* log_probs, int dtype, int64_t T_total, int64_t D, const void* cu_seqlens,
+                               const void* lengths, int64_t B, const void* targets, int64_t target_width,
+                               const void* target_lengths, int index_flags, int64_t max_target_length, int blank,
+                               int zero_infinity, int reduction, const void* grad_scale, void* grad_out,
+                               int checkpoint_interval, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Reduction of per-utterance losses ([PR] `ctc.py` `forward_packed`): SUM = sum of losses[b];
  * MEAN = mean over b of losses[b] / max(target_lengths[b], 1); B = 0 gives 0 (SUM) or NaN (MEAN).
  * Writes one float to *out (device).  NONE is PCTC_ERR_ARG.  Only the target-length bit of

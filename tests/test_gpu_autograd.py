@@ -8,6 +8,10 @@ capture, on the GPU, through the C ABI.
   absolute for float32 / 16-bit inputs); a second backward on the same forward state matches as
   well.
 - Autograd (`ctc_loss` + `.backward`) for none / sum / mean matches the oracle.
+- The forward that writes the gradient too (packed_ctc_forward_grad): with unit upstream weights the
+  update leaves it as the fused call wrote it (the same bytes, also through autograd's
+  `loss.backward()`); other weights rewrite it to the oracle's, and a later update with unit
+  weights rewrites it again; on both pipelines, at checkpoint interval 8 and for float64.
 - A captured graph of the fused call and one of the autograd forward + backward, with the target
   bound set to the targets width (no host read), replayed several times on fresh inputs with eager
   work between replays: every replay matches an eager call on the same inputs.
@@ -128,6 +132,73 @@ def test_autograd_vs_oracle(api, oracle_mod, reduction):
     if reduction != "none":
         np.testing.assert_allclose(float(out.detach().cpu()), ref["reduced"], rtol=1e-4)
     assert lp.grad.dtype == lp.dtype
+
+
+@pytest.mark.parametrize("case", ["small/streamed", "asr_bpe/grouped", "large_vocab/streamed", "small/K8",
+                                  "float64"])
+def test_forward_grad_and_update(api, oracle_mod, case):
+    _say(f"[gpu autograd] forward with the gradient, then updates: {case}")
+    name, how = case.split("/") if "/" in case else ("small", case)
+    b = W.make_workload(name)
+    if how == "float64":
+        b = W.make_batch([300, 41, 0, 170], [[1, 2, 2, 3], [4], [5], [6, 1, 6]], 9, seed=5, sigma=1.5, dtype="f64",
+                         reduction="mean")
+    lp = b.log_probs.to("cuda:0")
+    args = _dev_args(b)
+    K = 8 if how == "K8" else 1
+    kw = dict(blank=b.blank, zero_infinity=b.zero_infinity, reduction=b.reduction,
+              max_target_length=int(b.target_lengths.max()), checkpoint_interval=K)
+    old = api.pipeline()
+    api.set_pipeline("grouped" if how == "grouped" else "streamed")
+    try:
+        l0, r0, _ = api.packed_ctc_loss(lp, *args, **kw)
+        losses, reduced, grad, state = api.packed_ctc_forward_grad(lp, *args, **kw)
+        torch.cuda.synchronize()
+        assert api.last_call_status() == 0
+        assert torch.equal(losses, l0) and (reduced is None or torch.equal(reduced, r0)), case
+        unit_ref = oracle_mod.ctc_batch(b, reduction=b.reduction)
+        _check_oracle(losses, grad, unit_ref, lp.dtype, f"{case}/forward")
+        ones = torch.ones(b.B, dtype=losses.dtype)
+        first = grad.clone()
+        api.packed_ctc_backward_update(state, ones, grad, zero_infinity=b.zero_infinity)
+        torch.cuda.synchronize()
+        assert torch.equal(grad, first), f"{case}: a unit update changed the rows"
+        rng = np.random.default_rng(5)
+        gs = rng.uniform(-1.0, 1.0, size=b.B)
+        gs[0] = 0.0
+        api.packed_ctc_backward_update(state, torch.from_numpy(gs).to(losses.dtype), grad,
+                                       zero_infinity=b.zero_infinity)
+        torch.cuda.synchronize()
+        ref = oracle_mod.ctc_batch(b, reduction=b.reduction, grad_scale=gs)
+        _check_oracle(losses, grad, ref, lp.dtype, f"{case}/update")
+        # after other weights, unit weights rewrite the rows (the forward's are gone)
+        api.packed_ctc_backward_update(state, ones, grad, zero_infinity=b.zero_infinity)
+        torch.cuda.synchronize()
+        _check_oracle(losses, grad, unit_ref, lp.dtype, f"{case}/unit again")
+        assert api.last_call_status() == 0
+    finally:
+        api.set_pipeline(old)
+
+
+def test_autograd_unit_upstream_keeps_the_forward_rows(api, oracle_mod):
+    _say("[gpu autograd] loss.backward() with the forward's rows")
+    b = W.make_workload("large_vocab")
+    lp0 = b.log_probs.to("cuda:0")
+    kw = dict(blank=b.blank, zero_infinity=b.zero_infinity, reduction=b.reduction)
+    _, _, fused = api.packed_ctc_loss(lp0, *_dev_args(b), **kw)
+    lp = lp0.clone().requires_grad_(True)
+    out = api.ctc_loss(lp, *_dev_args(b), **kw)
+    out.backward()
+    torch.cuda.synchronize()
+    assert api.last_call_status() == 0
+    tol = TOL[lp.dtype][1]
+    assert float((lp.grad.double() - fused.double()).abs().max()) <= tol
+    ref = oracle_mod.ctc_batch(b)
+    _check_oracle(torch.from_numpy(ref["loss"]), lp.grad, ref, lp.dtype, "autograd/unit")
+    # a tensor that needs no gradient: the loss only
+    out2 = api.ctc_loss(lp0, *_dev_args(b), **kw)
+    torch.cuda.synchronize()
+    assert torch.allclose(out2, out.detach(), rtol=1e-6, atol=0)
 
 
 def _fresh_lp(b, k):

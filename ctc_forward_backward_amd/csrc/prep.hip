@@ -107,7 +107,8 @@ __global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers
 // a contiguous range of rows: the label ids of its utterance stay in registers from row to row,
 // and for U+1 <= 512 the values too, so the table row is written once.
 constexpr int kGLab = 8;  // label columns per lane held in registers
-static_assert(4 * 64 * kGLab * sizeof(float) <= kRowKernelLds, "the streamed gather's class-ordered rows use 64 kGLab floats of LDS per wave");
+// LDS per wave of the streamed gather's class-ordered rows: two rows of 64 kGLab floats
+constexpr size_t kGatherRowsLds = 2 * 64 * kGLab * sizeof(float);
 
 template <int DT>
 __device__ __forceinline__ float ld1(const void* p, int64_t i) {
@@ -115,6 +116,27 @@ __device__ __forceinline__ float ld1(const void* p, int64_t i) {
   else if constexpr (DT == kF64) return static_cast<float>(static_cast<const double*>(p)[i]);
   else if constexpr (DT == kF16) return static_cast<float>(static_cast<const _Float16*>(p)[i]);
   else return __builtin_bit_cast(float, static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+}
+
+// element c of a row that starts at `row` (uniform): a 32-bit offset from a uniform base, one register
+// per address; NT: non-temporal (the line is not kept in the caches)
+template <int DT, bool NT>
+__device__ __forceinline__ float ld_row(const void* row, int c) {
+  constexpr uint32_t esz = DT == kF64 ? 8 : (DT == kF32 ? 4 : 2);
+  const char* p = static_cast<const char*>(row) + static_cast<uint32_t>(c) * esz;  // (c >= 0: a zero-extended offset)
+  if constexpr (DT == kF32) {
+    const float* q = reinterpret_cast<const float*>(p);
+    return NT ? __builtin_nontemporal_load(q) : *q;
+  } else if constexpr (DT == kF64) {
+    const double* q = reinterpret_cast<const double*>(p);
+    return static_cast<float>(NT ? __builtin_nontemporal_load(q) : *q);
+  } else if constexpr (DT == kF16) {
+    const _Float16* q = reinterpret_cast<const _Float16*>(p);
+    return static_cast<float>(NT ? __builtin_nontemporal_load(q) : *q);
+  } else {
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(p);
+    return __builtin_bit_cast(float, static_cast<uint32_t>(NT ? __builtin_nontemporal_load(q) : *q) << 16);
+  }
 }
 
 // the same, non-temporal (the line is not kept in the caches)
@@ -291,6 +313,154 @@ __global__ void __launch_bounds__(256) gather_kernel(Inputs in, Layout L, Pointe
   }
 }
 
+// ---- the streamed gather, two rows at a time where they share an utterance ----
+
+// a row of a long target (U + 1 > 64 kGLab): two passes over its label columns in label order
+template <int DT>
+__device__ __forceinline__ void gather_row_long(const Inputs& in, const Layout& L, const Pointers& P, int64_t r, int b,
+                                             int U, int lane) {
+  constexpr int64_t esz = DT == kF64 ? 8 : (DT == kF32 ? 4 : 2);
+  const int* lab = P.lab + (int64_t)b * (L.Umax + 1);
+  const void* row = static_cast<const char*>(in.log_probs) + r * L.D * esz;
+  float* E = P.E + r * L.E_stride;
+  float mx = kNeg;
+  int nan = 0;
+  for (int j = lane; j <= U; j += 64) {
+    float x = ld_row<DT, false>(row, lab[j]) * kLog2e;
+    nan |= (x != x);
+    x = fmaxf(x, kNeg);
+    mx = fmaxf(mx, x);
+    E[j] = x;
+  }
+  mx = wave_max(mx);
+  const float off = mx > kNegHalf ? floorf(mx) : 0.0f;
+  for (int j = lane; j <= U; j += 64) E[j] -= off;  // (each lane its own entries)
+  if (lane == 0) {
+    P.rowoff[r] = static_cast<int>(off);
+    E[U + 1] = kNeg;  // the column of label states that do not exist
+    P.Eb[r] = E[0];   // (this lane wrote E[0] above)
+  }
+  if (nan) {
+    atomicOr(&P.meta[b].flags, kNanInput);
+    if (P.meta[b].flags & kNoAlignment) {  // its loss is NaN, not +inf (no recursion will say so)
+      P.nll[b] = (double)NAN;
+      P.w[b] = utterance_weight(in, L.B, b, false);
+    }
+  }
+}
+
+// The utterance's columns for a wave (one round trip: its label count, label ids or class bitmap,
+// label ranks): label order, lane i of load k takes label 64 k + i (the blank where there is none);
+// class order (SORTED), it takes the class of rank 64 k + i and dm holds each label's class rank.
+template <bool SORTED>
+__device__ __forceinline__ void gather_prepare(const Inputs& in, const Layout& L, const Pointers& P, int b,
+                                               GatherCur& g, int lane, float* wl) {
+  const int Umax = static_cast<int>(L.Umax);
+  int pre[kGLab];
+  if (SORTED) {
+    const int Dw = static_cast<int>(L.Dw);
+    const uint32_t* gb = P.cbits + (int64_t)b * Dw;
+    const int* gp = P.cpref + (int64_t)b * Dw;
+    const int* dmap = P.dmap + (int64_t)b * (Umax + 1);
+#pragma unroll
+    for (int k = 0; k < kGLab; ++k) pre[k] = dmap[min(lane + 64 * k, Umax)];  // (ranks past U: never used)
+    g.U = P.meta[b].U;
+    g.ncls = gp[Dw - 1] + __builtin_popcount(gb[Dw - 1]);
+    // the classes by rank: the bitmap's set bits in order, written at their ranks
+    for (int i = lane; i < Dw; i += 64) {
+      uint32_t bits = gb[i];
+      int k = gp[i];
+      while (bits) {
+        const int e = __builtin_ctz(bits);
+        bits &= bits - 1u;
+        wl[k++] = static_cast<float>(32 * i + e);  // (exact: class ids are below 2^24)
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int k = 0; k < kGLab; ++k) {
+      g.col[k] = static_cast<int>(wl[min(lane + 64 * k, g.ncls - 1)]);
+      g.dm[k] = pre[k];
+    }
+  } else {
+    const int* lab = P.lab + (int64_t)b * (Umax + 1);
+#pragma unroll
+    for (int k = 0; k < kGLab; ++k) pre[k] = lab[min(lane + 64 * k, Umax)];
+    g.U = P.meta[b].U;
+    g.ncls = g.U + 1;
+    g.lab = lab;
+#pragma unroll
+    for (int k = 0; k < kGLab; ++k) g.col[k] = lane + 64 * k <= g.U ? pre[k] : in.blank;  // (ids past U: stale)
+  }
+  g.b = b;
+}
+
+// NR (1 or 2) consecutive rows r .. r + NR - 1 of utterance g.b, U + 1 <= 64 kGLab: every load of
+// both rows in flight at once, then each row's offset and table row.  SORTED: class order with
+// non-temporal loads (see gather_row_sorted), the values put in label order through the wave's LDS
+// (wl: NR x 64 kGLab floats).
+template <int DT, bool SORTED, int NR>
+__device__ __forceinline__ void gather_rows(const Inputs& in, const Layout& L, const Pointers& P, int64_t r,
+                                            GatherCur& g, int lane, float* wl) {
+  const int U = g.U, n = g.ncls, b = g.b;
+  constexpr int64_t esz = DT == kF64 ? 8 : (DT == kF32 ? 4 : 2);
+  float v[NR][kGLab];
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const void* row = static_cast<const char*>(in.log_probs) + (r + j) * L.D * esz;
+#pragma unroll
+    for (int k = 0; k < kGLab; ++k) v[j][k] = ld_row<DT, SORTED>(row, g.col[k]);
+  }
+  int nan = 0;
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    float mx = kNeg;
+#pragma unroll
+    for (int k = 0; k < kGLab; ++k) {
+      const bool ok = lane + 64 * k < n;
+      float x = v[j][k] * kLog2e;
+      nan |= ok && (x != x);
+      x = fmaxf(x, kNeg);  // -inf (and NaN, flagged above) become the finite sentinel
+      v[j][k] = x;
+      if (ok) mx = fmaxf(mx, x);
+    }
+    mx = wave_max(mx);
+    const float off = mx > kNegHalf ? floorf(mx) : 0.0f;
+    float* E = P.E + (r + j) * L.E_stride;
+    float eb;
+    if (SORTED) {
+      // LDS operations of one wave complete in order: these writes follow the reads of this area's
+      // previous row (or of the class list) and precede the reads below
+      float* w = wl + j * (64 * kGLab);
+#pragma unroll
+      for (int k = 0; k < kGLab; ++k)
+        if (lane + 64 * k < n) w[lane + 64 * k] = v[j][k] - off;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int k = 0; k < kGLab; ++k)
+        if (lane + 64 * k <= U) E[lane + 64 * k] = w[g.dm[k]];
+      eb = w[g.dm[0]];
+    } else {
+#pragma unroll
+      for (int k = 0; k < kGLab; ++k)
+        if (lane + 64 * k <= U) E[lane + 64 * k] = v[j][k] - off;
+      eb = v[j][0] - off;
+    }
+    if (lane == 0) {
+      P.rowoff[r + j] = static_cast<int>(off);
+      E[U + 1] = kNeg;  // the column of label states that do not exist
+      P.Eb[r + j] = eb;
+    }
+  }
+  if (nan) {
+    atomicOr(&P.meta[b].flags, kNanInput);
+    if (P.meta[b].flags & kNoAlignment) {  // its loss is NaN, not +inf (no recursion will say so)
+      P.nll[b] = (double)NAN;
+      P.w[b] = utterance_weight(in, L.B, b, false);
+    }
+  }
+}
+
 // Streamed pipeline (one group): the rows in their natural order, each wave a contiguous share, its
 // rows' owners found 64 at a time (as row_owner does); rows owned by no utterance get a zero gradient
 // when `gaps` is given.
@@ -299,8 +469,11 @@ __global__ void __launch_bounds__(256) gather_kernel(Inputs in, Layout L, Pointe
 // SORTED: rows of up to 64 kGLab labels are read in class order (gather_row_sorted); taken for rows
 // of at least kSortedRowBytes, where it pays (on short rows the lines serve every load anyway, and
 // its registers cost occupancy: small and char_level 8 us slower)
-constexpr int64_t kSortedRowBytes = 4096;
-template <int DT, bool SORTED>
+// TWO: two rows of an utterance in flight at once, for rows of at least kTwoRowBytes (on shorter
+// rows the loads of one row are few and the second row's registers cost more occupancy than its
+// latency saves: small 1.7 us slower, asr_bpe 4.7 us faster)
+constexpr int64_t kSortedRowBytes = 4096, kTwoRowBytes = 1024;
+template <int DT, bool SORTED, bool TWO>
 __global__ void __launch_bounds__(256) gather_stream_kernel(Inputs in, Layout L, Pointers P, void* gaps, int sched,
                                                             int nhist, int ocap) {
   extern __shared__ __attribute__((aligned(16))) int gsh[];  // (at least 4 waves x 64 kGLab words)
@@ -314,8 +487,8 @@ __global__ void __launch_bounds__(256) gather_stream_kernel(Inputs in, Layout L,
   const int64_t wid = ((int64_t)blockIdx.x - first) * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t per = (L.T_total + waves - 1) / waves;
   const int64_t r0 = min(wid * per, L.T_total), r1 = min(r0 + per, L.T_total);
-  GatherCur g, gc;  // label-ordered and class-ordered rows
-  float* wl = reinterpret_cast<float*>(gsh) + (threadIdx.x >> 6) * (64 * kGLab);
+  GatherCur g;  // the utterance whose columns this wave holds
+  float* wl = reinterpret_cast<float*>(gsh) + (threadIdx.x >> 6) * (kGatherRowsLds / 4);
   for (int64_t q = r0; q < r1; q += 64) {
     const int n = static_cast<int>(min((int64_t)64, r1 - q));
     int own = lane < n ? P.rowmap[q + lane] : -1;
@@ -325,14 +498,25 @@ __global__ void __launch_bounds__(256) gather_stream_kernel(Inputs in, Layout L,
       const Meta m = P.meta[own];
       if (q + lane < m.start || q + lane >= (int64_t)m.start + m.T) own = -1;
     }
-    for (int i = 0; i < n; ++i) {
+    for (int i = 0; i < n;) {  // (everything wave-uniform)
       const int b = __builtin_amdgcn_readlane(own, i);
-      if (b >= 0) {
-        if (SORTED && P.meta[b].U < 64 * kGLab) gather_row_sorted<DT>(in, L, P, q + i, b, gc, lane, wl);
-        else gather_row<DT>(in, L, P, q + i, b, g, lane);  // (wave-uniform)
-      } else if (gaps) {
-        rows::fill_row<DT>(L, gaps, q + i, 0.0f, lane);
+      if (b < 0) {
+        if (gaps) rows::fill_row<DT>(L, gaps, q + i, 0.0f, lane);
+        ++i;
+        continue;
       }
+      // a new utterance: its columns, taken as if its target were short (the loads stay in bounds either
+      // way); a long target (U + 1 > 64 kGLab) goes row by row in label order (gather_row, cursor gl)
+      if (b != g.b) gather_prepare<SORTED>(in, L, P, b, g, lane, wl);
+      if (g.U >= 64 * kGLab) {
+        gather_row_long<DT>(in, L, P, q + i, b, g.U, lane);
+        ++i;
+        continue;
+      }
+      const bool two = TWO && i + 1 < n && __builtin_amdgcn_readlane(own, i + 1) == b;
+      if (two) gather_rows<DT, SORTED, 2>(in, L, P, q + i, g, lane, wl);
+      else gather_rows<DT, SORTED, 1>(in, L, P, q + i, g, lane, wl);
+      i += two ? 2 : 1;
     }
   }
 }
@@ -960,7 +1144,9 @@ hipError_t launch_gather_stream(const Inputs& in, const Layout& L, const Pointer
   // as in the grouped gather: 16 workgroups per compute unit, each wave a contiguous share of the
   // rows (plus the schedule's workgroup)
   const int grid = 16 * (cus > 0 ? cus : 256) + (gs.on ? 1 : 0);
-  const size_t lds = gs.on ? gs.lds : kRowKernelLds;
+  const bool sorted = L.D * (in.dtype == kF32 ? 4 : 2) >= kSortedRowBytes;
+  // (class-ordered rows: two rows' values per wave in LDS)
+  const size_t lds = std::max(gs.on ? gs.lds : kRowKernelLds, sorted ? 4 * kGatherRowsLds : 0);
   auto go = [&](auto kern) {
     if (lds > 48 * 1024) {
       hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -970,11 +1156,16 @@ hipError_t launch_gather_stream(const Inputs& in, const Layout& L, const Pointer
     kern<<<grid, 256, lds, s>>>(in, L, P, gaps, gs.on ? 1 : 0, gs.nhist, gs.ocap);
     return hipGetLastError();
   };
-  const bool sorted = L.D * (in.dtype == kF32 ? 4 : 2) >= kSortedRowBytes;
-  if (in.dtype == kF32) return sorted ? go(&gather_stream_kernel<kF32, true>) : go(&gather_stream_kernel<kF32, false>);
-  if (in.dtype == kF64) return go(&gather_stream_kernel<kF64, false>);
-  if (in.dtype == kF16) return sorted ? go(&gather_stream_kernel<kF16, true>) : go(&gather_stream_kernel<kF16, false>);
-  return sorted ? go(&gather_stream_kernel<kBF16, true>) : go(&gather_stream_kernel<kBF16, false>);
+  const bool two = L.D * (in.dtype == kF32 ? 4 : 2) >= kTwoRowBytes;
+  if (in.dtype == kF32)
+    return sorted ? go(&gather_stream_kernel<kF32, true, true>)
+                  : (two ? go(&gather_stream_kernel<kF32, false, true>) : go(&gather_stream_kernel<kF32, false, false>));
+  if (in.dtype == kF64) return go(&gather_stream_kernel<kF64, false, false>);
+  if (in.dtype == kF16)
+    return sorted ? go(&gather_stream_kernel<kF16, true, true>)
+                  : (two ? go(&gather_stream_kernel<kF16, false, true>) : go(&gather_stream_kernel<kF16, false, false>));
+  return sorted ? go(&gather_stream_kernel<kBF16, true, true>)
+                : (two ? go(&gather_stream_kernel<kBF16, false, true>) : go(&gather_stream_kernel<kBF16, false, false>));
 }
 
 hipError_t launch_classes(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {

@@ -22,7 +22,8 @@ __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
 
 // One workgroup per utterance: clamp the metadata so that every later access stays in bounds,
 // write the U+1 distinct class ids of the extended label sequence, claim the utterance's rows.
-__device__ __forceinline__ void class_maps(const Layout& L, const Pointers& P, int b, uint32_t* cw, int* wsum);
+__device__ __forceinline__ void class_maps(const Layout& L, const Pointers& P, int b, uint32_t* cw, int* wsum,
+                                           const int* lab);
 __device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int groups, int bands, int* sh, int nhist,
                               int ocap);
 
@@ -60,6 +61,10 @@ __global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers
   __syncthreads();
   const Meta mm = m;
   int* lab = P.lab + (int64_t)b * (L.Umax + 1);
+  // classes (the streamed pipeline's setup): the labels are kept in LDS too, after the class maps'
+  // 2 Dw words, and read back from there
+  extern __shared__ __attribute__((aligned(16))) uint32_t pcw[];
+  int* sl = reinterpret_cast<int*>(pcw + 2 * L.Dw);
   const bool t64 = in.index_flags & 4;
   for (int j = threadIdx.x; j <= mm.U; j += blockDim.x) {
     int64_t c = in.blank;
@@ -69,7 +74,9 @@ __global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers
       if (c >= L.D) c = L.D - 1;
     }
     lab[j] = static_cast<int>(c);
+    if (classes) sl[j] = static_cast<int>(c);
   }
+  const int* lr = classes ? sl : lab;
   for (int t = threadIdx.x; t < mm.T; t += blockDim.x) P.rowmap[mm.start + t] = b;
   // No alignment fits when the utterance has fewer frames than its labels need: one frame per label
   // and a blank frame between two equal neighbours (the skip is barred between equal ids).  Such an
@@ -80,7 +87,7 @@ __global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers
   if (mm.U > 0 && mm.T < 2 * mm.U - 1) {  // uniform
     __syncthreads();  // (also: this workgroup's label writes above are visible to its loads below)
     int rep = 0;
-    for (int j = threadIdx.x + 1; j < mm.U; j += blockDim.x) rep += lab[j + 1] == lab[j];
+    for (int j = threadIdx.x + 1; j < mm.U; j += blockDim.x) rep += lr[j + 1] == lr[j];
     if (rep) atomicAdd(&repeats, rep);
     __syncthreads();
   }
@@ -93,10 +100,9 @@ __global__ void __launch_bounds__(256) prep_kernel(Inputs in, Layout L, Pointers
     P.llb[b] = -(double)INFINITY;
     P.w[b] = utterance_weight(in, L.B, b, true);
   }
-  if (classes) {  // the class maps of this utterance (its labels were written above, by this workgroup)
-    extern __shared__ __attribute__((aligned(16))) uint32_t pcw[];
+  if (classes) {  // the class maps of this utterance (its labels are in LDS)
     __shared__ int wsum[4];
-    class_maps(L, P, b, pcw, wsum);
+    class_maps(L, P, b, pcw, wsum, sl);
   }
 }
 
@@ -525,11 +531,12 @@ __global__ void __launch_bounds__(256) gather_stream_kernel(Inputs in, Layout L,
 // its labels), the number of classes before each bitmap word, and for each label index j the rank
 // of lab[j] among the present classes.  The gradient rows add each class's posterior at its
 // column through these ranks.  cw: 2 Dw words of LDS.
-__device__ __forceinline__ void class_maps(const Layout& L, const Pointers& P, int b, uint32_t* cw, int* wsum) {
+// lab: the utterance's U + 1 labels (LDS in the prep launch, the workspace copy otherwise)
+__device__ __forceinline__ void class_maps(const Layout& L, const Pointers& P, int b, uint32_t* cw, int* wsum,
+                                           const int* lab) {
   const int tid = threadIdx.x;
   const int Dw = static_cast<int>(L.Dw);
   const int U = P.meta[b].U;
-  const int* lab = P.lab + (int64_t)b * (L.Umax + 1);
   for (int i = tid; i < Dw; i += 256) cw[i] = 0u;
   __syncthreads();
   for (int j = tid; j <= U; j += 256) atomicOr(&cw[lab[j] >> 5], 1u << (lab[j] & 31));
@@ -575,7 +582,7 @@ __global__ void __launch_bounds__(256) classes_kernel(Layout L, Pointers P) {
   if (skipped(P)) return;
   extern __shared__ uint32_t cw[];  // Dw bitmap words, then Dw prefix counts
   __shared__ int wsum[4];
-  class_maps(L, P, blockIdx.x, cw, wsum);
+  class_maps(L, P, blockIdx.x, cw, wsum, P.lab + (int64_t)blockIdx.x * (L.Umax + 1));
 }
 
 // Losses after zero_infinity, gradient weights and the sum / mean reduction (one workgroup,
@@ -1101,7 +1108,7 @@ hipError_t launch_prep(const Inputs& in, const Layout& L, const Pointers& P, hip
   // (row_owner tells the others).
   const int64_t ring_words = setup ? 2 * 2 * L.Gmax * L.T_total : 0;
   if (L.B > 0) {
-    const size_t lds = setup ? 2 * sizeof(uint32_t) * (size_t)L.Dw : 0;
+    const size_t lds = setup ? sizeof(uint32_t) * (2 * (size_t)L.Dw + (size_t)L.Umax + 1) : 0;
     if (lds > 48 * 1024) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prep_kernel),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));

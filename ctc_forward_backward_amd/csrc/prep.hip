@@ -145,19 +145,9 @@ __device__ __forceinline__ float ld_row(const void* row, int c) {
   }
 }
 
-// the same, non-temporal (the line is not kept in the caches)
-template <int DT>
-__device__ __forceinline__ float ld1_nt(const void* p, int64_t i) {
-  if constexpr (DT == kF32) return __builtin_nontemporal_load(static_cast<const float*>(p) + i);
-  else if constexpr (DT == kF64) return static_cast<float>(__builtin_nontemporal_load(static_cast<const double*>(p) + i));
-  else if constexpr (DT == kF16) return static_cast<float>(__builtin_nontemporal_load(static_cast<const _Float16*>(p) + i));
-  else
-    return __builtin_bit_cast(float, static_cast<uint32_t>(__builtin_nontemporal_load(static_cast<const uint16_t*>(p) + i))
-                                         << 16);
-}
 
 // The label ids of the utterance a wave is on (kept while its rows follow one another); in the
-// class-ordered form (gather_row_sorted), the utterance's classes in increasing order and the rank
+// class-ordered form (gather_rows, SORTED), the utterance's classes in increasing order and the rank
 // of each label's class instead
 struct GatherCur {
   int b = -1, U = 0, ncls = 0;
@@ -165,84 +155,6 @@ struct GatherCur {
   int col[kGLab];
   int dm[kGLab];
 };
-
-// Streamed pipeline, U + 1 <= 64 kGLab: the row's values at the utterance's distinct classes, read
-// in increasing column order (lane i of load k takes the class of rank 64 k + i), so that each
-// 128-byte line is requested by one load, and with non-temporal loads: the log probs are read again
-// only by the gradient rows, much later, and their lines kept in the caches would displace the
-// emission table written here, which the recursions read next (large_vocab: the stream launch
-// 16 us faster; with the values read in label order, where one line serves several loads, the
-// non-temporal form fetched lines again and the gather took 30 us longer).  The values go to the
-// label order through the wave's LDS (wl: 64 kGLab floats).  Uses the class maps (class_maps).
-template <int DT>
-__device__ __forceinline__ void gather_row_sorted(const Inputs& in, const Layout& L, const Pointers& P, int64_t r,
-                                                  int b, GatherCur& g, int lane, float* wl) {
-  if (b != g.b) {
-    // the classes by rank: the bitmap's set bits in order, written at their ranks
-    const int Dw = static_cast<int>(L.Dw);
-    const uint32_t* gb = P.cbits + (int64_t)b * Dw;
-    const int* gp = P.cpref + (int64_t)b * Dw;
-    g.U = P.meta[b].U;
-    g.ncls = gp[Dw - 1] + __builtin_popcount(gb[Dw - 1]);
-    for (int i = lane; i < Dw; i += 64) {
-      uint32_t bits = gb[i];
-      int k = gp[i];
-      while (bits) {
-        const int e = __builtin_ctz(bits);
-        bits &= bits - 1u;
-        wl[k++] = static_cast<float>(32 * i + e);  // (exact: class ids are below 2^24)
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    const int* dmap = P.dmap + (int64_t)b * (L.Umax + 1);
-#pragma unroll
-    for (int k = 0; k < kGLab; ++k) {
-      g.col[k] = static_cast<int>(wl[min(lane + 64 * k, g.ncls - 1)]);
-      g.dm[k] = dmap[min(lane + 64 * k, g.U)];
-    }
-    g.b = b;
-  }
-  const int U = g.U, n = g.ncls;
-  float* E = P.E + r * L.E_stride;
-  const int64_t row = r * L.D;
-  float v[kGLab];
-#pragma unroll
-  for (int k = 0; k < kGLab; ++k) v[k] = ld1_nt<DT>(in.log_probs, row + g.col[k]);  // all loads in flight
-  float mx = kNeg;
-  int nan = 0;
-#pragma unroll
-  for (int k = 0; k < kGLab; ++k) {
-    const bool ok = lane + 64 * k < n;
-    float x = v[k] * kLog2e;
-    nan |= ok && (x != x);
-    x = fmaxf(x, kNeg);  // -inf (and NaN, flagged above) become the finite sentinel
-    v[k] = x;
-    if (ok) mx = fmaxf(mx, x);
-  }
-  mx = wave_max(mx);
-  const float off = mx > kNegHalf ? floorf(mx) : 0.0f;
-  // LDS operations of one wave complete in order: these writes follow the reads of the previous
-  // row (or of the class list) and precede the reads below
-#pragma unroll
-  for (int k = 0; k < kGLab; ++k)
-    if (lane + 64 * k < n) wl[lane + 64 * k] = v[k] - off;
-  __builtin_amdgcn_wave_barrier();
-#pragma unroll
-  for (int k = 0; k < kGLab; ++k)
-    if (lane + 64 * k <= U) E[lane + 64 * k] = wl[g.dm[k]];
-  if (lane == 0) {
-    P.rowoff[r] = static_cast<int>(off);
-    E[U + 1] = kNeg;          // the column of label states that do not exist
-    P.Eb[r] = wl[g.dm[0]];    // the blank's value (label 0)
-  }
-  if (nan) {
-    atomicOr(&P.meta[b].flags, kNanInput);
-    if (P.meta[b].flags & kNoAlignment) {  // its loss is NaN, not +inf (no recursion will say so)
-      P.nll[b] = (double)NAN;
-      P.w[b] = utterance_weight(in, L.B, b, false);
-    }
-  }
-}
 
 template <int DT>
 __device__ __forceinline__ void gather_row(const Inputs& in, const Layout& L, const Pointers& P, int64_t r, int b,
@@ -402,9 +314,15 @@ __device__ __forceinline__ void gather_prepare(const Inputs& in, const Layout& L
 }
 
 // NR (1 or 2) consecutive rows r .. r + NR - 1 of utterance g.b, U + 1 <= 64 kGLab: every load of
-// both rows in flight at once, then each row's offset and table row.  SORTED: class order with
-// non-temporal loads (see gather_row_sorted), the values put in label order through the wave's LDS
-// (wl: NR x 64 kGLab floats).
+// both rows in flight at once, then each row's offset and table row.
+// SORTED: the values at the utterance's distinct classes, read in increasing column order (lane i of
+// load k takes the class of rank 64 k + i), so that each 128-byte line is requested by one load,
+// and with non-temporal loads: the log probs are read again only by the gradient rows, much later,
+// and their lines kept in the caches would displace the emission table written here, which the
+// recursions read next (large_vocab: the stream launch 16 us faster; with the values read in label
+// order, where one line serves several loads, the non-temporal form fetched lines again and the
+// gather took 30 us longer).  The values go to the label order through the wave's LDS (wl: NR x
+// 64 kGLab floats) and the rank of each label's class (the class maps, class_maps).
 template <int DT, bool SORTED, int NR>
 __device__ __forceinline__ void gather_rows(const Inputs& in, const Layout& L, const Pointers& P, int64_t r,
                                             GatherCur& g, int lane, float* wl) {
@@ -472,7 +390,7 @@ __device__ __forceinline__ void gather_rows(const Inputs& in, const Layout& L, c
 // when `gaps` is given.
 // With sched (nhist, ocap: see schedule_body), workgroup 0 builds the schedule instead, beside the
 // gathering workgroups: it reads only what prep wrote, and nothing here reads what it writes.
-// SORTED: rows of up to 64 kGLab labels are read in class order (gather_row_sorted); taken for rows
+// SORTED: rows of up to 64 kGLab labels are read in class order (gather_rows); taken for rows
 // of at least kSortedRowBytes, where it pays (on short rows the lines serve every load anyway, and
 // its registers cost occupancy: small and char_level 8 us slower)
 // TWO: two rows of an utterance in flight at once, for rows of at least kTwoRowBytes (on shorter

@@ -605,9 +605,11 @@ __device__ __forceinline__ void wait_steps(const int* prog, int steps, int64_t t
 // alignment has weight 0), and after any give-up the rows are NaN.
 // POST (a split forward): the band's rows get their class sums over z in P.post instead (the weights
 // come with the backward, whose gradient rows apply them).  RB: row chunks per lane in flight.
+// sums (not POST): the rows' class sums go to P.post as well (a forward whose gradient a later
+// update may form again with other weights: packed_ctc_forward_grad).
 template <int DT, bool POST, int RB>
 __device__ __forceinline__ void row_band(const Inputs& in, const Layout& L, const Pointers& P, void* grad,
-                                         uint32_t* lds, int b, int k, int w, int lane, int& cur_b) {
+                                         uint32_t* lds, int b, int k, int w, int lane, int& cur_b, int sums) {
   const Meta m = P.meta[b];
   const int T = m.T;
   const int band = band_frames(L, T);
@@ -646,7 +648,20 @@ __device__ __forceinline__ void row_band(const Inputs& in, const Layout& L, cons
   for (int i = w; i < n; i += kStreamWaves) {
     const int t = i < n1 ? ra + i : lo2 + (i - n1);
     const int64_t r = (int64_t)m.start + t;
-    if (live && rows::posterior_stream(L, P, acc, r, b, w0, lane)) rows::dense_row<DT, true, RB>(in, L, P, grad, lds, r, b, w0, lane, cur_b);
+    bool ok = false;
+    if (live && sums) {
+      // the sums over z alone to P.post (0 where the frame has no mass), then weighted in LDS
+      ok = rows::posterior_stream(L, P, acc, r, b, 1.0f, lane);
+      float* out = P.post + r * L.C_stride;
+      for (int c = lane; c <= m.U; c += 64) {
+        const float v = ok ? acc[c] : 0.0f;
+        out[c] = v;
+        acc[c] = v * w0;
+      }
+    } else if (live) {
+      ok = rows::posterior_stream(L, P, acc, r, b, w0, lane);
+    }
+    if (ok) rows::dense_row<DT, true, RB>(in, L, P, grad, lds, r, b, w0, lane, cur_b);
     else rows::fill_row<DT>(L, grad, r, fill, lane);
   }
 }
@@ -659,8 +674,8 @@ __device__ __forceinline__ void row_band(const Inputs& in, const Layout& L, cons
 // POST: a split forward (see row_band); the backward then skips its posterior pass.
 template <int DT, bool POST, int RB>
 __global__ void __launch_bounds__(64 * kStreamWaves, 1) stream_workers(Inputs in, Layout L, Pointers P, void* grad,
-                                                                       int per_wave) {
-  if (POST && blockIdx.x == 0 && threadIdx.x == 0) P.ctl->post_ready = 1;
+                                                                       int per_wave, int sums) {
+  if ((POST || sums) && blockIdx.x == 0 && threadIdx.x == 0) P.ctl->post_ready = 1;
   extern __shared__ __attribute__((aligned(16))) unsigned char ssm[];
   Shared& sh = *reinterpret_cast<Shared*>(ssm);
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -690,7 +705,7 @@ __global__ void __launch_bounds__(64 * kStreamWaves, 1) stream_workers(Inputs in
   while (idx < qlen + nbands) {
     const int2 bd = P.bands[idx - qlen];
     row_band<DT, POST, RB>(in, L, P, grad, lds, __builtin_amdgcn_readfirstlane(bd.x), __builtin_amdgcn_readfirstlane(bd.y),
-                       w, lane, cur_b);
+                       w, lane, cur_b, sums);
     __syncthreads();
     if (tid == 0) sh.item = atomicAdd(&q->qcount, 1);
     __syncthreads();
@@ -734,7 +749,8 @@ bool stream_fits(const Inputs& in, const Layout& L) {
   return in.dtype != kF64 && L.B > 0 && L.B <= 2048 && L.T_total > 0 && L.D > 0 && stream_lds(L) <= 150 * 1024;
 }
 
-hipError_t launch_stream(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s) {
+hipError_t launch_stream(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s,
+                         bool sums) {
   if (!stream_fits(in, L)) return hipErrorInvalidValue;
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -747,7 +763,7 @@ hipError_t launch_stream(const Inputs& in, const Layout& L, const Pointers& P, v
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (err != hipSuccess) return err;
-    kernel<<<cus > 0 ? cus : 256, 64 * kStreamWaves, lds, s>>>(in, L, P, grad_out, per_wave);
+    kernel<<<cus > 0 ? cus : 256, 64 * kStreamWaves, lds, s>>>(in, L, P, grad_out, per_wave, sums && grad_out ? 1 : 0);
     return hipGetLastError();
   };
   // without a gradient (a split forward) the rows' class sums only: no log-prob row is read, so one

@@ -164,7 +164,7 @@ struct Pointers {
   uint32_t* cbits;  // (B, Dw) bitmap of the classes present
   int* cpref;       // (B, Dw) number of classes present in the words before each word
   int* dmap;        // (B, Umax + 1) rank among the present classes of lab[j]
-  float* post;      // (T_total, C_stride) per row: the class sums times w / z, by class rank
+  float* post;      // (T_total, C_stride) per row: the class sums over z (without the weight), by class rank
   // streamed pipeline: per (utterance, direction) the recursion steps whose states every block has
   // stored where any compute unit sees them, and the queue of row bands (utterance, band), readiest
   // first
@@ -520,7 +520,9 @@ hipError_t launch_dense(const Inputs& in, const Layout& L, const Pointers& P, vo
 // streamed pipeline (one group): the queue of row bands, then one persistent launch running the
 // recursions and, as their frames become ready, the posteriors and gradient rows
 bool stream_fits(const Inputs& in, const Layout& L);
-hipError_t launch_stream(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s);
+// sums (with grad_out): each row's class sums are kept in P.post too, for a later gradient update
+hipError_t launch_stream(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s,
+                         bool sums = false);
 // float64 inputs in float64 arithmetic (f64.hip): alpha of every utterance (stored in the state region
 // as float64) and its loss; then beta with each frame's posteriors and gradient row (needs the
 // weights and the class maps)

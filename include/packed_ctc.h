@@ -217,8 +217,9 @@ int packed_ctc_backward(const void* log_probs, int dtype, int64_t T_total, int64
  *
  * packed_ctc_forward_grad: losses_out, reduced_out and grad_out exactly as packed_ctc_loss with
  *   grad_scale = NULL (w_b from the reduction and zero_infinity alone), and the workspace left
- *   holding what packed_ctc_backward reads, with a record that grad_out holds the rows for unit
- *   upstream weights under this zero_infinity and reduction.  max_target_length must be >= 0
+ *   holding what packed_ctc_backward reads (with the streamed pipeline: every row's class sums, as
+ *   packed_ctc_forward leaves them), with a record that grad_out holds the rows for unit upstream
+ *   weights under this zero_infinity and reduction.  max_target_length must be >= 0
  *   (PCTC_ERR_ARG otherwise).  Other arguments as for packed_ctc_loss.
  * packed_ctc_backward_update: grad_out as packed_ctc_backward writes it, with one difference: when
  *   every grad_scale[b] is exactly 1 (or grad_scale is NULL) and zero_infinity and reduction are

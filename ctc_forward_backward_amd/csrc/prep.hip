@@ -284,11 +284,12 @@ __device__ __forceinline__ void gather_prepare(const Inputs& in, const Layout& L
     for (int k = 0; k < kGLab; ++k) pre[k] = dmap[min(lane + 64 * k, Umax)];  // (ranks past U: never used)
     g.U = P.meta[b].U;
     g.ncls = gp[Dw - 1] + __builtin_popcount(gb[Dw - 1]);
-    // the classes by rank: the bitmap's set bits in order, written at their ranks
+    // the classes by rank: the bitmap's set bits in order, written at their ranks (the first
+    // 64 kGLab: a longer target is gathered by gather_row_long, and the wave's LDS holds no more)
     for (int i = lane; i < Dw; i += 64) {
       uint32_t bits = gb[i];
       int k = gp[i];
-      while (bits) {
+      while (bits && k < 64 * kGLab) {
         const int e = __builtin_ctz(bits);
         bits &= bits - 1u;
         wl[k++] = static_cast<float>(32 * i + e);  // (exact: class ids are below 2^24)

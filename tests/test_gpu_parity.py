@@ -323,10 +323,10 @@ def test_wide_rows_class_and_label_order(api, oracle_mod, dtype, D):
     # utterances, next to each other so that waves pass from one kind to the other
     _say(f"[gpu parity] wide rows, both gather orders ({dtype}, D = {D})")
     rng = np.random.default_rng(21)
-    lengths = [1500, 640, 7, 900]
-    tl = [700, 300, 0, 511]
+    lengths = [1500, 640, 7, 900, 3100]
+    tl = [700, 300, 0, 511, 1500]  # (the last: more classes than a wave's LDS list holds)
     targets = [[int(x) for x in rng.integers(1, D, size=u)] for u in tl]
-    b = W.make_batch(lengths, targets, D, seed=21, sigma=3.0, dtype=dtype, reduction="sum", gaps=[0, 0, 1, 0])
+    b = W.make_batch(lengths, targets, D, seed=21, sigma=3.0, dtype=dtype, reduction="sum", gaps=[0, 0, 1, 0, 0])
     ref = oracle_mod.ctc_batch(b)
     got = run_gpu(api, b)
     compare(got, ref, torch.float16 if dtype == "f16" else torch.float32, f"wide rows {dtype}")

@@ -281,7 +281,7 @@ __device__ __forceinline__ void gather_prepare(const Inputs& in, const Layout& L
     const int* gp = P.cpref + (int64_t)b * Dw;
     const int* dmap = P.dmap + (int64_t)b * (Umax + 1);
 #pragma unroll
-    for (int k = 0; k < kGLab; ++k) pre[k] = dmap[min(lane + 64 * k, Umax)];  // (ranks past U: never used)
+    for (int k = 0; k < kGLab; ++k) pre[k] = dmap[min(lane + 64 * k, Umax)];
     g.U = P.meta[b].U;
     g.ncls = gp[Dw - 1] + __builtin_popcount(gb[Dw - 1]);
     // the classes by rank: the bitmap's set bits in order, written at their ranks (the first
@@ -299,7 +299,7 @@ __device__ __forceinline__ void gather_prepare(const Inputs& in, const Layout& L
 #pragma unroll
     for (int k = 0; k < kGLab; ++k) {
       g.col[k] = static_cast<int>(wl[min(lane + 64 * k, g.ncls - 1)]);
-      g.dm[k] = pre[k];
+      g.dm[k] = lane + 64 * k <= g.U ? pre[k] : 0;  // (ranks past U: stale; every LDS read stays in bounds)
     }
   } else {
     const int* lab = P.lab + (int64_t)b * (Umax + 1);

@@ -124,3 +124,20 @@ def test_long_targets_at_the_checkpoint_limit(api, oracle_mod):
         t2 = [[int(x) for x in rng.integers(1, 50, size=1024)]]
         b2 = W.make_batch([2100], t2, 50, seed=18)
         api.packed_ctc_loss(*_dev(b2), blank=0, checkpoint_interval=16)
+
+
+def test_block_classes_in_one_batch(api, oracle_mod):
+    # targets on both sides of each boundary of the 1-4 / 5-8 / 9-16 state-block classes (a target of
+    # U labels takes (U + 64) // 64 blocks), in one batch and in a mixed order, at K = 8 and 4
+    _say("[gpu checkpoint] every block class in one batch")
+    rng = np.random.default_rng(23)
+    ulist = [255, 0, 511, 256, 1023, 512, 40, 700, 191]
+    lengths = [2 * u + 40 for u in ulist]
+    targets = [[int(x) for x in rng.integers(1, 60, size=u)] for u in ulist]
+    b = W.make_batch(lengths, targets, 60, seed=23, sigma=1.5, reduction="none")
+    args = _dev(b)
+    ref = oracle_mod.ctc_batch(b)
+    for K in (8, 4):
+        losses, _, grad = api.packed_ctc_loss(*args, blank=0, reduction="none", checkpoint_interval=K)
+        torch.cuda.synchronize()
+        _check(losses, grad, ref, torch.float32, f"block classes K={K}")

@@ -30,14 +30,6 @@ namespace pctc {
 
 namespace {
 
-// a workgroup barrier that orders LDS only: the loads fetched ahead stay in flight across it (the
-// kernel shares nothing between its waves through global memory)
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // NW waves per workgroup, NB state blocks per wave: wave w holds the blocks w, w + NW, w + 2 NW, ...
 // (a short target spreads over the waves, a long one gives each wave several blocks to interleave)
 template <int NW, int NB>

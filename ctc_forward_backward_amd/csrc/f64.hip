@@ -11,11 +11,21 @@
 // row are formed as beta passes it: gradient = w * (exp(lp) - posterior summed per class)).
 //
 // Design (precision first; the float32 / 16-bit inputs take the pipelined kernels):
-//   - one workgroup per utterance; the S = 2U+1 states are split into contiguous ranges of at least
-//     two states over up to 1024 threads, each range in registers; per frame every thread publishes
-//     its two edge states in a double-buffered LDS array and reads its neighbour's, one barrier per
-//     frame;
-//   - natural-log space, log-sum-exp as max + log1p(exp(-|a - b|)) with HIP's float64 exp / log1p;
+//   - one workgroup per utterance, of 256, 512 or 1024 threads by the call's longest target; the
+//     S = 2U+1 states are split into contiguous ranges of at least two states, each range in
+//     registers; per frame every thread publishes its two edge states in a double-buffered LDS array
+//     and reads its neighbour's;
+//   - what a frame reads (emissions, the stored alpha, the first columns of the gradient row) does
+//     not depend on the recursion and is fetched a frame ahead where the registers allow it (four
+//     states per thread in alpha, under 1024 threads in beta); the frames' barriers order LDS only, so those loads and the alpha and
+//     gradient stores stay in flight across them; the beta side takes two barriers per frame (one
+//     after the posteriors are added into the class sums, one after the gradient row), with the
+//     class sums in two copies by frame parity, and takes each state's posterior relative to the
+//     likelihood (at most 1) before normalising by the frame's own total;
+//   - natural-log space, with HIP's float64 exp / log1p: a state's update is one three-term
+//     log-sum-exp, the largest term plus log1p of the sum of the other two's exponentials relative
+//     to it (the third term -inf where the skip is not allowed); alpha computes every slot of a
+//     thread's range with no branch, so that the slots' chains interleave;
 //   - alpha is stored in float64 in the workspace's state region (T_total rows of Gmax * 128
 //     doubles); beta is not stored: the second kernel forms each frame's posteriors from the stored
 //     alpha and its own beta, normalised by the frame's own total (the posteriors of a frame sum to
@@ -28,11 +38,12 @@ namespace pctc {
 
 namespace {
 
-constexpr int kT64 = 1024;   // threads per workgroup
-// PER, a kernel's template argument: states a thread holds at most (each thread holds ceil or floor
-// of S / n states, n = min(1024, S / 2)): 4 for S <= 4096, 8 for S <= 8192, 16 up to 16383 =
-// 2 * 8191 + 1.  The register arrays take PER entries, so the smallest that fits the call's target
-// bound is launched (16 for every call kept the arrays' registers and spilled them).
+constexpr int kT64 = 1024;   // threads per workgroup, at most
+// PER and NT, a kernel's template arguments: states a thread holds at most (each thread holds ceil
+// or floor of S / n states, n = min(NT, S / 2)) and the workgroup's threads: PER 4 for S <= 4096
+// (NT 256 up to S = 512, 512 up to 1024, else 1024), 8 for S <= 8192, 16 up to 16383 = 2 * 8191 + 1.
+// The register arrays take PER entries, so the smallest that fits the call's target bound is
+// launched (16 for every call kept the arrays' registers and spilled them).
 constexpr double kNegInf = -INFINITY;
 
 __device__ __forceinline__ double lse2d(double a, double b) {
@@ -41,17 +52,28 @@ __device__ __forceinline__ double lse2d(double a, double b) {
   return hi + log1p(exp(lo - hi));
 }
 
+// log(e^a + e^b + e^c) with no branch: the largest plus log1p of the other two relative to it (both
+// exponentials at once, then one log1p: the depth of a two-term log-sum-exp); a term at -inf adds
+// nothing, and all three at -inf give -inf
+__device__ __forceinline__ double lse3d(double a, double b, double c) {
+  const double hi = fmax(a, b), lo = fmin(a, b);
+  const double m = fmax(hi, c), mid = fmin(hi, c);
+  const double ref = m > kNegInf ? m : 0.0;
+  return m + log1p(exp(lo - ref) + exp(mid - ref));
+}
+
 // state split of an utterance with S states over n threads: thread i holds [lo, hi), at least two
 // states each (except a single state when S = 1)
 struct Split {
   int n, lo, hi;
 };
 
-__device__ __forceinline__ int threads_for(int S) { return S < 2 ? 1 : min(kT64, S / 2); }
+__device__ __forceinline__ int threads_for(int S, int nt) { return S < 2 ? 1 : min(nt, S / 2); }
 
-__device__ __forceinline__ Split split_of(int S, int tid) {
+// (nt: the workgroup's threads)
+__device__ __forceinline__ Split split_of(int S, int tid, int nt) {
   Split sp;
-  sp.n = threads_for(S);
+  sp.n = threads_for(S, nt);
   sp.lo = (int)((int64_t)S * tid / sp.n);
   sp.hi = (int)((int64_t)S * (tid + 1) / sp.n);
   return sp;
@@ -87,12 +109,12 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
 
 __device__ __forceinline__ bool block_any(bool v, double* red) { return block_sum(v ? 1.0 : 0.0, red) > 0.0; }
 
-// Alpha of utterance blockIdx.x (launched with 1024 threads; threads beyond the split idle at the
+// Alpha of utterance blockIdx.x (launched with NT threads; threads beyond the split idle at the
 // barriers), the loss, and the NaN flag of the emissions it read.  Workgroup 0 also clears the
 // health word (this path has no waits on other workgroups).
-template <int PER>
-__global__ void __launch_bounds__(kT64) f64_alpha_kernel(Inputs in, Layout L, Pointers P) {
-  __shared__ double bnd[2][kT64][2];
+template <int PER, int NT>
+__global__ void __launch_bounds__(NT) f64_alpha_kernel(Inputs in, Layout L, Pointers P) {
+  __shared__ double bnd[2][NT][2];
   __shared__ double red[32];
   const int b = blockIdx.x, tid = threadIdx.x;
   if (b == 0 && tid == 0) P.ctl->err = 0;
@@ -104,7 +126,7 @@ __global__ void __launch_bounds__(kT64) f64_alpha_kernel(Inputs in, Layout L, Po
     return;
   }
   const int* lab = P.lab + (int64_t)b * (L.Umax + 1);
-  const Split sp = split_of(S, tid);
+  const Split sp = split_of(S, tid, NT);
   const bool active = tid < sp.n;
   const int cnt = active ? sp.hi - sp.lo : 0;
   const int64_t Ss = L.Gmax * 128, D = L.D;
@@ -126,30 +148,49 @@ __global__ void __launch_bounds__(kT64) f64_alpha_kernel(Inputs in, Layout L, Po
     }
     if (k < cnt) A[m.start * Ss + s] = a[k];
   }
+  // a frame's emissions do not depend on the recursion: fetched one frame ahead (every thread loads,
+  // at a valid column), and the frame's barrier orders LDS only, so neither these loads nor the
+  // alpha stores are waited for at it
+  double en[PER];
+  auto fetch = [&](int t) {
+    const int64_t r = m.start + t;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) en[k] = ld_lp(in.log_probs, r * D + cls[k]);
+  };
+  // (ahead only with four states per thread: with more, the second set of registers spills)
+  constexpr bool kAhead = PER == 4;
+  if (kAhead && T > 1) fetch(1);
   for (int t = 1; t < T; ++t) {
     const int buf = t & 1;
     const int64_t r = m.start + t;
+    if (!kAhead) fetch(t);
+    double ec[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) ec[k] = en[k];
+    if (kAhead && t + 1 < T) fetch(t + 1);
     if (active) {  // the two highest states of this range at t-1
       bnd[buf][tid][0] = cnt >= 1 ? a[cnt - 1] : kNegInf;
       bnd[buf][tid][1] = cnt >= 2 ? a[cnt - 2] : kNegInf;
     }
-    __syncthreads();
+    lds_barrier();
     if (active) {
-      // alpha[t-1] at lo-1 and lo-2 (the previous range holds at least two states)
-      double p1 = tid > 0 ? bnd[buf][tid - 1][0] : kNegInf;
-      double p2 = tid > 0 ? bnd[buf][tid - 1][1] : kNegInf;
+      // alpha[t-1] at lo-1 and lo-2 (the previous range holds at least two states); every slot of
+      // the range is computed, with no branch, so that the slots' chains interleave (a slot past the
+      // range computes from -inf and is not kept)
+      const double p1 = tid > 0 ? bnd[buf][tid - 1][0] : kNegInf;
+      const double p2 = tid > 0 ? bnd[buf][tid - 1][1] : kNegInf;
+      double na[PER];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const double s1 = k == 0 ? p1 : a[k - 1], s2 = k == 0 ? p2 : (k == 1 ? p1 : a[k - 2]);
+        na[k] = lse3d(a[k], s1, skip[k] ? s2 : kNegInf) + ec[k];
+      }
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
         if (k < cnt) {
-          const double cur = a[k];
-          double v = lse2d(cur, p1);
-          if (skip[k]) v = lse2d(v, p2);
-          const double e = ld_lp(in.log_probs, r * D + cls[k]);
-          nan |= e != e;
-          a[k] = v + e;
+          nan |= ec[k] != ec[k];
+          a[k] = na[k];
           A[r * Ss + sp.lo + k] = a[k];
-          p2 = p1;
-          p1 = cur;
         }
       }
     }
@@ -172,12 +213,13 @@ __global__ void __launch_bounds__(kT64) f64_alpha_kernel(Inputs in, Layout L, Po
 }
 
 // Beta of utterance blockIdx.x and, as it passes each frame, the frame's posteriors (from the stored
-// alpha) and its gradient row.  acc: (Umax + 1) doubles of LDS (dynamic), the class sums by rank.
-template <int PER>
-__global__ void __launch_bounds__(kT64) f64_beta_rows_kernel(Inputs in, Layout L, Pointers P, double* grad) {
+// alpha) and its gradient row.  acc: (Umax + 1) doubles of LDS (dynamic), the class sums by rank, or
+// twice that when two is set.
+template <int PER, int NT>
+__global__ void __launch_bounds__(NT) f64_beta_rows_kernel(Inputs in, Layout L, Pointers P, double* grad, int two) {
   if (skipped(P)) return;
   extern __shared__ double acc[];
-  __shared__ double bnd[2][kT64][2];
+  __shared__ double bnd[2][NT][2];
   __shared__ double red[32];
   const int b = blockIdx.x, tid = threadIdx.x;
   const Meta m = P.meta[b];
@@ -196,7 +238,7 @@ __global__ void __launch_bounds__(kT64) f64_beta_rows_kernel(Inputs in, Layout L
   const int* dmap = P.dmap + (int64_t)b * (L.Umax + 1);
   const uint32_t* cbits = P.cbits + (int64_t)b * L.Dw;
   const int* cpref = P.cpref + (int64_t)b * L.Dw;
-  const Split sp = split_of(S, tid);
+  const Split sp = split_of(S, tid, NT);
   const bool active = tid < sp.n;
   const int cnt = active ? sp.hi - sp.lo : 0;
   const double* A = reinterpret_cast<const double*>(P.ABa);
@@ -212,124 +254,194 @@ __global__ void __launch_bounds__(kT64) f64_beta_rows_kernel(Inputs in, Layout L
     skip[k] = k < cnt && (s & 1) && s + 2 < S && lab[(s + 1) >> 1] != lab[(s + 3) >> 1];
     bt[k] = kNegInf;
   }
-  for (int i = tid; i <= U; i += blockDim.x) acc[i] = 0.0;
+  // the class sums by rank, in two copies taken by frame parity when the LDS holds both (then one
+  // barrier fewer per frame: a frame fills one copy while the other is cleared)
+  const int64_t Cs = L.Umax + 1;
+  const bool dual = two;
+  for (int i = tid; i < (dual ? 2 * Cs : Cs); i += blockDim.x) acc[i] = 0.0;
+  const int dblank = dmap[0];
+  const double ll = -nll;  // the log likelihood: every state's posterior is at most 1 relative to it
+  const int lane = tid & 63, wv = tid >> 6, nw = (blockDim.x + 63) >> 6;
+  // what a frame reads (its emissions at the states' classes, the stored alpha, the first gradient
+  // column of the thread) does not depend on beta: fetched for frame t-1 as soon as frame t has
+  // used it (every thread loads, at valid addresses), and the frame's barriers order LDS only, so
+  // these loads run under frame t's barriers and gradient row, and the gradient stores are not
+  // waited for at them
+  // (below 1024 threads) the thread's first GC columns of the gradient row: their class rank (-1: no
+  // class; the class bitmap does not change between frames) and the next frame's log probabilities
+  constexpr int GC = NT < kT64 ? 8 : 1;
+  double lq[PER], aq[PER], gq[GC];
+  int rk[GC];
+#pragma unroll
+  for (int j = 0; j < GC; ++j) {
+    const int64_t c = min((int64_t)tid + (int64_t)j * NT, D - 1);
+    const int wi = (int)(c >> 5);
+    const uint32_t bits = cbits[wi];
+    rk[j] = (bits >> (c & 31)) & 1u ? cpref[wi] + __builtin_popcount(bits & ((1u << (c & 31)) - 1u)) : -1;
+  }
+  auto fetch_states = [&](int t) {
+    const int64_t r = m.start + t;
+    const double* lp = static_cast<const double*>(in.log_probs) + r * D;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      lq[k] = lp[cls[k]];
+      aq[k] = A[r * Ss + min(sp.lo + k, S - 1)];
+    }
+  };
+  auto fetch_col = [&](int t) {
+    const double* lp = static_cast<const double*>(in.log_probs) + (m.start + t) * D;
+#pragma unroll
+    for (int j = 0; j < GC; ++j) gq[j] = lp[min((int64_t)tid + (int64_t)j * NT, D - 1)];
+  };
+  // (ahead only below 1024 threads: at that register budget the loads ahead spill)
+  constexpr bool kAhead = NT < kT64;
+  if (kAhead) {
+    fetch_states(T - 1);
+    fetch_col(T - 1);
+  }
+  __syncthreads();
   for (int t = T - 1; t >= 0; --t) {
     const int64_t r = m.start + t;
     const double* lp = static_cast<const double*>(in.log_probs) + r * D;
+    const int par = t & 1;
+    double* cs = acc + (dual ? par * Cs : 0);
+    // a state's emission and alpha at frame t: fetched ahead, or read here
+    auto emis = [&](int k) { if constexpr (kAhead) return lq[k]; else return lp[cls[k]]; };
+    auto alph = [&](int k) { if constexpr (kAhead) return aq[k]; else return A[r * Ss + sp.lo + k]; };
     // beta at t (emission of frame t included)
     if (t == T - 1) {
 #pragma unroll
       for (int k = 0; k < PER; ++k)
-        if (k < cnt && sp.lo + k >= S - 2) bt[k] = lp[cls[k]];
-    } else {
-      const int buf = t & 1;
-      if (active) {  // the two lowest states of this range at t+1
-        bnd[buf][tid][0] = cnt >= 1 ? bt[0] : kNegInf;
-        bnd[buf][tid][1] = cnt >= 2 ? bt[1] : kNegInf;
-      }
-      __syncthreads();
-      if (active) {
-        // beta[t+1] at hi and hi+1 (the next range holds at least two states)
-        const bool last = tid + 1 >= sp.n;
-        double n1 = last ? kNegInf : bnd[buf][tid + 1][0];
-        double n2 = last ? kNegInf : bnd[buf][tid + 1][1];
+        if (k < cnt && sp.lo + k >= S - 2) bt[k] = emis(k);
+    } else if (active) {
+      // beta[t+1] at hi and hi+1, as the next range left them (it holds at least two states)
+      const bool last = tid + 1 >= sp.n;
+      const double n1 = last ? kNegInf : bnd[par ^ 1][tid + 1][0];
+      const double n2 = last ? kNegInf : bnd[par ^ 1][tid + 1][1];
+      // (the range's own states one after another: here the frame's posteriors and gradient row,
+      // not this chain, set the pace, and computing every slot costs more than it saves)
+      double s1 = n1, s2 = n2;
 #pragma unroll
-        for (int k = PER - 1; k >= 0; --k) {
-          if (k < cnt) {
-            const double cur = bt[k];
-            double v = lse2d(cur, n1);
-            if (skip[k]) v = lse2d(v, n2);
-            bt[k] = v + lp[cls[k]];
-            n2 = n1;
-            n1 = cur;
-          }
+      for (int k = PER - 1; k >= 0; --k) {
+        if (k < cnt) {
+          const double cur = bt[k];
+          bt[k] = lse3d(cur, s1, skip[k] ? s2 : kNegInf) + emis(k);
+          s2 = s1;
+          s1 = cur;
         }
       }
     }
-    // posteriors of frame t: alpha + beta - lp per state, normalised by the frame's own total
-    double e[PER];
-    double mx = kNegInf;
+    if (active) {  // the two lowest states of this range at t, for frame t-1
+      bnd[par][tid][0] = cnt >= 1 ? bt[0] : kNegInf;
+      bnd[par][tid][1] = cnt >= 2 ? bt[1] : kNegInf;
+    }
+    // posteriors of frame t: alpha + beta - lp per state relative to the likelihood; label states
+    // add into their class's sum, the blank states (all one class) are summed per wave first; the
+    // frame's own total normalises them when the row is written
+    double x[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      e[k] = kNegInf;
-      if (k < cnt) {
-        const double ak = A[r * Ss + sp.lo + k];
-        if (ak > kNegInf && bt[k] > kNegInf) e[k] = ak + bt[k] - lp[cls[k]];
-        mx = fmax(mx, e[k]);
-      }
+      const double ak = k < cnt ? alph(k) : kNegInf;
+      x[k] = k < cnt && ak > kNegInf && bt[k] > kNegInf ? ak + bt[k] - emis(k) - ll : kNegInf;
     }
-    mx = block_max(mx, red);
-    double z = 0.0;
+    double z = 0.0, bsum = 0.0;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      if (k < cnt && e[k] > kNegInf) {
-        e[k] = exp(e[k] - mx);
-        z += e[k];
-      } else {
-        e[k] = 0.0;
+      if (x[k] > kNegInf) {
+        const double e = exp(x[k]);
+        z += e;
+        if ((sp.lo + k) & 1) atomicAdd(&cs[rank[k]], e);
+        else bsum += e;
       }
     }
-    z = block_sum(z, red);  // (its barriers also order the zeroed class sums before the adds)
-    const double scale = z > 0.0 ? w / z : 0.0;
-    // label states add into their class's sum; the blank states (all one class) are summed per
-    // thread first
-    double bsum = 0.0;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      if (k < cnt && e[k] != 0.0) {
-        if ((sp.lo + k) & 1) atomicAdd(&acc[rank[k]], e[k] * scale);
-        else bsum += e[k] * scale;
-      }
+    if (kAhead && t > 0) fetch_states(t - 1);
+    for (int o = 32; o > 0; o >>= 1) {
+      z += __shfl_xor(z, o);
+      bsum += __shfl_xor(bsum, o);
     }
-    if (bsum != 0.0) atomicAdd(&acc[dmap[0]], bsum);
-    __syncthreads();
+    if (lane == 0) {
+      red[wv] = z;
+      if (bsum != 0.0) atomicAdd(&cs[dblank], bsum);
+    }
+    lds_barrier();
+    double ztot = 0.0;
+    for (int i = 0; i < nw; ++i) ztot += red[i];  // fixed order: reproducible
+    const double scale = ztot > 0.0 ? w / ztot : 0.0;
     // the gradient row: w exp(lp) minus the class sum at the columns that carry a class
     double* g = grad + r * D;
-    for (int64_t c = tid; c < D; c += blockDim.x) {
+    int64_t c0 = tid;
+    if constexpr (kAhead) {
+#pragma unroll
+      for (int j = 0; j < GC; ++j) {
+        const int64_t c = (int64_t)tid + (int64_t)j * NT;
+        if (c < D) g[c] = w * exp(gq[j]) - (rk[j] >= 0 ? cs[rk[j]] * scale : 0.0);
+      }
+      c0 += (int64_t)GC * NT;
+    }
+    for (int64_t c = c0; c < D; c += NT) {
       const int wi = (int)(c >> 5);
       const uint32_t bits = cbits[wi];
       double v = w * exp(lp[c]);
-      if ((bits >> (c & 31)) & 1u) v -= acc[cpref[wi] + __builtin_popcount(bits & ((1u << (c & 31)) - 1u))];
+      if ((bits >> (c & 31)) & 1u) v -= cs[cpref[wi] + __builtin_popcount(bits & ((1u << (c & 31)) - 1u))] * scale;
       g[c] = v;
     }
-    __syncthreads();
-    for (int i = tid; i <= U; i += blockDim.x) acc[i] = 0.0;
+    if (kAhead && t > 0) fetch_col(t - 1);
+    lds_barrier();  // (the sums and the totals are read; this frame's copy is cleared for frame t-2)
+    for (int i = tid; i <= U; i += blockDim.x) cs[i] = 0.0;
+    if (!dual) lds_barrier();  // one copy: cleared before frame t-1 adds into it
   }
 }
 
 }  // namespace
 
-// states per thread of the longest target the call allows
-int per_thread(const Layout& L) {
+// states per thread (PER) and threads per workgroup (NT) of the longest target the call allows:
+// every thread holds at least two states, at most PER; a short target takes a smaller workgroup
+// (fewer waves in each frame's barriers, and a larger register budget per thread)
+struct F64Shape {
+  int per, nt;
+};
+
+F64Shape f64_shape(const Layout& L) {
   const int64_t S = 2 * L.Umax + 1;
-  return S <= 4096 ? 4 : (S <= 8192 ? 8 : 16);
+  if (S <= 512) return {4, 256};
+  if (S <= 1024) return {4, 512};
+  if (S <= 4096) return {4, kT64};
+  return {S <= 8192 ? 8 : 16, kT64};
 }
 
 hipError_t launch_f64_alpha(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(L.B > 0 ? L.B : 1);
-  const int per = per_thread(L);
-  if (per == 4) f64_alpha_kernel<4><<<grid, kT64, 0, s>>>(in, L, P);
-  else if (per == 8) f64_alpha_kernel<8><<<grid, kT64, 0, s>>>(in, L, P);
-  else f64_alpha_kernel<16><<<grid, kT64, 0, s>>>(in, L, P);
+  const F64Shape sh = f64_shape(L);
+  if (sh.nt == 256) f64_alpha_kernel<4, 256><<<grid, 256, 0, s>>>(in, L, P);
+  else if (sh.nt == 512) f64_alpha_kernel<4, 512><<<grid, 512, 0, s>>>(in, L, P);
+  else if (sh.per == 4) f64_alpha_kernel<4, kT64><<<grid, kT64, 0, s>>>(in, L, P);
+  else if (sh.per == 8) f64_alpha_kernel<8, kT64><<<grid, kT64, 0, s>>>(in, L, P);
+  else f64_alpha_kernel<16, kT64><<<grid, kT64, 0, s>>>(in, L, P);
   return hipGetLastError();
 }
 
 hipError_t launch_f64_beta_rows(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s) {
   if (L.B == 0 || L.T_total == 0 || L.D == 0) return hipGetLastError();
-  const size_t lds = sizeof(double) * (size_t)(L.Umax + 1);
-  auto launch = [&](auto kernel) {
+  const F64Shape sh = f64_shape(L);
+  // two copies of the class sums when they fit beside the kernel's static LDS (the boundary
+  // exchange, 32 B per thread, and the wave totals)
+  const size_t stat = 32 * (size_t)sh.nt + 256;
+  const bool two = 2 * sizeof(double) * (size_t)(L.Umax + 1) + stat <= 160 * 1024;
+  const size_t lds = (two ? 2 : 1) * sizeof(double) * (size_t)(L.Umax + 1);
+  auto launch = [&](auto kernel, int nt) {
     if (lds > 48 * 1024) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
       if (e != hipSuccess) return e;
     }
-    kernel<<<static_cast<unsigned>(L.B), kT64, lds, s>>>(in, L, P, static_cast<double*>(grad_out));
+    kernel<<<static_cast<unsigned>(L.B), nt, lds, s>>>(in, L, P, static_cast<double*>(grad_out), two ? 1 : 0);
     return hipGetLastError();
   };
-  const int per = per_thread(L);
-  if (per == 4) return launch(&f64_beta_rows_kernel<4>);
-  if (per == 8) return launch(&f64_beta_rows_kernel<8>);
-  return launch(&f64_beta_rows_kernel<16>);
+  if (sh.nt == 256) return launch(&f64_beta_rows_kernel<4, 256>, 256);
+  if (sh.nt == 512) return launch(&f64_beta_rows_kernel<4, 512>, 512);
+  if (sh.per == 4) return launch(&f64_beta_rows_kernel<4, kT64>, kT64);
+  if (sh.per == 8) return launch(&f64_beta_rows_kernel<8, kT64>, kT64);
+  return launch(&f64_beta_rows_kernel<16, kT64>, kT64);
 }
 
 }  // namespace pctc

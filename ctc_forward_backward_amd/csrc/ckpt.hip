@@ -33,7 +33,7 @@ namespace {
 // NW waves per workgroup, NB state blocks per wave: wave w holds the blocks w, w + NW, w + 2 NW, ...
 // (a short target spreads over the waves, a long one gives each wave several blocks to interleave)
 template <int NW, int NB>
-__global__ void __launch_bounds__(64 * NW) ckpt_posterior_kernel(Layout L, Pointers P) {
+__global__ void __launch_bounds__(64 * NW) ckpt_posterior_kernel(Layout L, Pointers P, int group) {
   if (skipped(P)) return;
   constexpr int NJ = NW * NB;
   extern __shared__ float cacc[];  // 2 x C_stride floats: a row's class sums by rank, by step parity
@@ -75,8 +75,10 @@ __global__ void __launch_bounds__(64 * NW) ckpt_posterior_kernel(Layout L, Point
     const int qb = P.qbase[b], cb0 = P.cbase[b];
     const double lsh = P.lsh[b], nll = P.nll[b];
     const float wgt = P.w[b];
-    // (uniform) a zero weight or an infinite loss: the gradient kernel fills these rows
-    if (wgt == 0.0f || !(nll < (double)INFINITY)) continue;
+    const int gb = P.gid[b];
+    // (uniform) a zero weight or an infinite loss: the gradient kernel fills these rows; another
+    // group's utterance: its own launch takes it
+    if (wgt == 0.0f || !(nll < (double)INFINITY) || (group >= 0 && gb != group)) continue;
     const int U = m.U, G = (U + 64) >> 6, T = m.T;
     // the likelihood as an integer and a fraction in [0, 1): the offsets are integers, so a state's
     // shift off + ob - lsh is formed exactly in integers and rounded once
@@ -254,7 +256,7 @@ __global__ void __launch_bounds__(64 * NW) ckpt_posterior_kernel(Layout L, Point
 
 }  // namespace
 
-hipError_t launch_ckpt_posteriors(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {
+hipError_t launch_ckpt_posteriors(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s) {
   (void)in;
   if (L.T_total == 0 || L.B == 0) return hipGetLastError();
   const size_t lds = 2 * sizeof(float) * (size_t)L.C_stride;
@@ -266,7 +268,7 @@ hipError_t launch_ckpt_posteriors(const Inputs& in, const Layout& L, const Point
                                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
       if (e != hipSuccess) return e;
     }
-    kern<<<g, 64 * nw, lds, s>>>(L, P);
+    kern<<<g, 64 * nw, lds, s>>>(L, P, group);
     return hipGetLastError();
   };
   // four waves; each holds up to four of the (at most 16) blocks

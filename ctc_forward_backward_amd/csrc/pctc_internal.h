@@ -64,7 +64,7 @@ struct Layout {
   int64_t K;         // checkpoint interval of alpha: every K-th step kept (1: every step)
   int64_t band;      // streamed pipeline: frames a side per row band of a long utterance (by the row's bytes)
   int64_t NQ;        // alpha rows kept per block: T_total (K = 1), else >= sum over utterances of ceil(T / K)
-  size_t off_qbase, off_cbase, off_cbits, off_cpref, off_dmap, off_meta, off_lab, off_rowmap, off_rowoff, off_E, off_Eb, off_AB, off_nll, off_llb, off_lsh, off_w, off_post, off_order, off_cum, off_ring,
+  size_t off_qbase, off_cbase, off_cbits, off_cpref, off_dmap, off_meta, off_lab, off_rowmap, off_rowoff, off_E, off_Eb, off_AB, off_nll, off_llb, off_lsh, off_w, off_post, off_order, off_cum, off_gid, off_ring,
       off_sig, off_items, off_ctl, off_prog, off_bands, total;
 };
 
@@ -159,6 +159,7 @@ struct Pointers {
   int* items;    // (2 B Gmax) queued recursion segments, by group: (utterance * 2 + direction) << 12 | segment
   int* order;    // (B) utterances by frame count, longest first (ties by index)
   int* cum;      // (B) per sorted position: rows of the group's earlier utterances
+  int* gid;      // (B) per utterance: its group
   ChainCtl* ctl;
   // classes of each utterance's extended labels (blank and labels), for the gradient rows:
   uint32_t* cbits;  // (B, Dw) bitmap of the classes present
@@ -528,8 +529,9 @@ hipError_t launch_stream(const Inputs& in, const Layout& L, const Pointers& P, v
 // weights and the class maps)
 hipError_t launch_f64_alpha(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
 hipError_t launch_f64_beta_rows(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s);
-// alpha checkpointing (ckpt.hip): every row's class sums from alpha recomputed out of the kept steps
-hipError_t launch_ckpt_posteriors(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s);
+// alpha checkpointing (ckpt.hip): the class sums of the rows of group `group` (-1: every row) from alpha
+// recomputed out of the kept steps
+hipError_t launch_ckpt_posteriors(const Inputs& in, const Layout& L, const Pointers& P, int group, hipStream_t s);
 // zero gradient rows owned by no utterance
 hipError_t launch_gaps(const Inputs& in, const Layout& L, const Pointers& P, void* grad_out, hipStream_t s);
 hipError_t launch_reduce(const float* losses, const void* target_lengths, bool i64, int64_t B, int reduction, float* out,

@@ -812,6 +812,7 @@ __device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int 
       int g = 0;
       while (g + 1 < groups && gfirst[g + 1] <= i) ++g;
       P.cum[i] = cT[i] - cT[gfirst[g]];
+      P.gid[b] = g;
       if (sT[b] == 0 || sU[b] < 0) continue;
       int n = cS[i];
       if (((sU[b] + 1 + 63) >> 6) <= 2) {
@@ -857,6 +858,7 @@ __device__ void schedule_body(const Layout& L, const Pointers& P, int sort, int 
           for (int i = p0; i < p1; ++i) {
             const Meta m = P.meta[i];
             P.cum[i] = rows;
+            P.gid[i] = g;
             rows += m.T;
             if (m.T == 0) continue;
             const int nseg = nseg_of(m.U, m.flags);

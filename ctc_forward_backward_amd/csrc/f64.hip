@@ -11,7 +11,7 @@
 // row are formed as beta passes it: gradient = w * (exp(lp) - posterior summed per class)).
 //
 // Design (precision first; the float32 / 16-bit inputs take the pipelined kernels):
-//   - one workgroup per utterance, of 256, 512 or 1024 threads by the call's longest target; the
+//   - one workgroup per utterance, of 512 or 1024 threads by the call's longest target; the
 //     S = 2U+1 states are split into contiguous ranges of at least two states, each range in
 //     registers; per frame every thread publishes its two edge states in a double-buffered LDS array
 //     and reads its neighbour's;
@@ -41,7 +41,7 @@ namespace {
 constexpr int kT64 = 1024;   // threads per workgroup, at most
 // PER and NT, a kernel's template arguments: states a thread holds at most (each thread holds ceil
 // or floor of S / n states, n = min(NT, S / 2)) and the workgroup's threads: PER 4 for S <= 4096
-// (NT 256 up to S = 512, 512 up to 1024, else 1024), 8 for S <= 8192, 16 up to 16383 = 2 * 8191 + 1.
+// (NT 512 up to S = 1024, else 1024), 8 for S <= 8192, 16 up to 16383 = 2 * 8191 + 1.
 // The register arrays take PER entries, so the smallest that fits the call's target bound is
 // launched (16 for every call kept the arrays' registers and spilled them).
 constexpr double kNegInf = -INFINITY;
@@ -262,13 +262,12 @@ __global__ void __launch_bounds__(NT) f64_beta_rows_kernel(Inputs in, Layout L, 
   const int dblank = dmap[0];
   const double ll = -nll;  // the log likelihood: every state's posterior is at most 1 relative to it
   const int lane = tid & 63, wv = tid >> 6, nw = (blockDim.x + 63) >> 6;
-  // what a frame reads (its emissions at the states' classes, the stored alpha, the first gradient
-  // column of the thread) does not depend on beta: fetched for frame t-1 as soon as frame t has
-  // used it (every thread loads, at valid addresses), and the frame's barriers order LDS only, so
-  // these loads run under frame t's barriers and gradient row, and the gradient stores are not
-  // waited for at them
-  // (below 1024 threads) the thread's first GC columns of the gradient row: their class rank (-1: no
-  // class; the class bitmap does not change between frames) and the next frame's log probabilities
+  // What a frame reads (its emissions at the states' classes, the stored alpha, the thread's first
+  // GC columns of the gradient row) does not depend on beta: below 1024 threads it is fetched for
+  // frame t-1 as soon as frame t has used it (every thread loads, at valid addresses), and the
+  // frame's barriers order LDS only, so these loads run under frame t's barriers and gradient row,
+  // and the gradient stores are not waited for at them.  The class rank of each of those GC columns
+  // (-1: no class) is found once: the class bitmap does not change between frames.
   constexpr int GC = NT < kT64 ? 8 : 1;
   double lq[PER], aq[PER], gq[GC];
   int rk[GC];
@@ -395,15 +394,15 @@ __global__ void __launch_bounds__(NT) f64_beta_rows_kernel(Inputs in, Layout L, 
 }  // namespace
 
 // states per thread (PER) and threads per workgroup (NT) of the longest target the call allows:
-// every thread holds at least two states, at most PER; a short target takes a smaller workgroup
-// (fewer waves in each frame's barriers, and a larger register budget per thread)
+// every thread holds at least two states, at most PER; a target of up to 511 labels takes 512
+// threads (a larger register budget per thread, for the loads fetched ahead; 256 threads measured
+// 3% slower: fewer waves share the gradient row)
 struct F64Shape {
   int per, nt;
 };
 
 F64Shape f64_shape(const Layout& L) {
   const int64_t S = 2 * L.Umax + 1;
-  if (S <= 512) return {4, 256};
   if (S <= 1024) return {4, 512};
   if (S <= 4096) return {4, kT64};
   return {S <= 8192 ? 8 : 16, kT64};
@@ -412,8 +411,7 @@ F64Shape f64_shape(const Layout& L) {
 hipError_t launch_f64_alpha(const Inputs& in, const Layout& L, const Pointers& P, hipStream_t s) {
   const unsigned grid = static_cast<unsigned>(L.B > 0 ? L.B : 1);
   const F64Shape sh = f64_shape(L);
-  if (sh.nt == 256) f64_alpha_kernel<4, 256><<<grid, 256, 0, s>>>(in, L, P);
-  else if (sh.nt == 512) f64_alpha_kernel<4, 512><<<grid, 512, 0, s>>>(in, L, P);
+  if (sh.nt == 512) f64_alpha_kernel<4, 512><<<grid, 512, 0, s>>>(in, L, P);
   else if (sh.per == 4) f64_alpha_kernel<4, kT64><<<grid, kT64, 0, s>>>(in, L, P);
   else if (sh.per == 8) f64_alpha_kernel<8, kT64><<<grid, kT64, 0, s>>>(in, L, P);
   else f64_alpha_kernel<16, kT64><<<grid, kT64, 0, s>>>(in, L, P);
@@ -437,7 +435,6 @@ hipError_t launch_f64_beta_rows(const Inputs& in, const Layout& L, const Pointer
     kernel<<<static_cast<unsigned>(L.B), nt, lds, s>>>(in, L, P, static_cast<double*>(grad_out), two ? 1 : 0);
     return hipGetLastError();
   };
-  if (sh.nt == 256) return launch(&f64_beta_rows_kernel<4, 256>, 256);
   if (sh.nt == 512) return launch(&f64_beta_rows_kernel<4, 512>, 512);
   if (sh.per == 4) return launch(&f64_beta_rows_kernel<4, kT64>, kT64);
   if (sh.per == 8) return launch(&f64_beta_rows_kernel<8, kT64>, kT64);

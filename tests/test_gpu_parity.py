@@ -410,9 +410,9 @@ def test_float64_inputs(api, oracle_mod, reduction):
 @pytest.mark.parametrize("U,D,gtol", [(100, 2500, None), (255, 64, None), (256, 64, None), (511, 64, None),
                                       (600, 64, None), (2100, 64, None), (4100, 64, 2e-10)])
 def test_float64_workgroup_shapes(api, oracle_mod, U, D, gtol):
-    """float64 at each workgroup shape the longest target selects (256 threads up to 255 labels, 512
-    up to 511, then 1024 threads of 4, 8 or 16 states) and on both sides of each boundary, beside a
-    short utterance; D = 2500 runs the gradient row past the columns a thread keeps in registers."""
+    """float64 at each workgroup shape the longest target selects (512 threads up to 511 labels, then
+    1024 threads of 4, 8 or 16 states) and on both sides of each boundary, beside a short utterance;
+    D = 2500 runs the gradient row past the columns a thread keeps in registers."""
     _say(f"[gpu parity] float64 workgroup shape: U = {U}, D = {D}")
     rng = np.random.default_rng(40 + U)
     targets = [[int(x) for x in rng.integers(1, D, size=U)], [int(x) for x in rng.integers(1, D, size=5)]]

@@ -141,3 +141,39 @@ def test_block_classes_in_one_batch(api, oracle_mod):
         losses, _, grad = api.packed_ctc_loss(*args, blank=0, reduction="none", checkpoint_interval=K)
         torch.cuda.synchronize()
         _check(losses, grad, ref, torch.float32, f"block classes K={K}")
+
+
+def test_graph_capture_checkpointed_groups(api):
+    # a checkpointed call on a batch large enough to run in length-sorted groups on the library's
+    # streams, captured in a graph after an eager call; each replay with fresh log probs (and eager
+    # calls between replays) matches the eager call
+    _say("[gpu checkpoint] graph capture of a grouped checkpointed call")
+    b = W.make_workload("asr_bpe")
+    dev = torch.device("cuda:0")
+    args = _dev(b)[1:]
+    kw = dict(blank=b.blank, zero_infinity=b.zero_infinity, reduction=b.reduction,
+              max_target_length=int(b.targets.shape[1]), checkpoint_interval=8)
+    lp_static = b.log_probs.to(dev).clone()
+    api.packed_ctc_loss(lp_static, *args, **kw)  # eager first: the library's group streams exist
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        losses, reduced, grad = api.packed_ctc_loss(lp_static, *args, **kw)
+    gen = torch.Generator(device=dev)
+    for k in range(3):
+        gen.manual_seed(200 + k)
+        x = torch.randn(tuple(lp_static.shape), device=dev, generator=gen) * 2.0
+        fresh = torch.log_softmax(x, dim=1).to(lp_static.dtype)
+        lp_static.copy_(fresh)
+        graph.replay()
+        torch.cuda.synchronize()
+        el, er, eg = api.packed_ctc_loss(fresh, *args, **kw)  # eager work between replays
+        torch.cuda.synchronize()
+        assert api.last_call_status() == 0
+        fin = torch.isfinite(el)
+        assert torch.equal(torch.isfinite(losses), fin), k
+        assert torch.allclose(losses[fin], el[fin], rtol=1e-6, atol=0), k
+        assert torch.allclose(reduced, er, rtol=1e-6, atol=0, equal_nan=True), k
+        assert torch.equal(torch.isnan(grad), torch.isnan(eg)), k
+        assert float((grad.double() - eg.double()).nan_to_num().abs().max()) <= 1e-6, k
+        _say(f"  replay {k}: matches the eager call")

@@ -224,6 +224,9 @@ def parse():
                          "leg): the run a profiler traces")
     ap.add_argument("--pipeline", default="streamed", choices=["streamed", "grouped"],
                     help="pipeline of the timed calls (the other one is timed too, for context)")
+    ap.add_argument("--checkpoint-interval", type=int, default=1,
+                    help="alpha checkpoint interval K of the timed calls (K > 1 runs the grouped pipeline); "
+                         "for profiling that path, not the headline line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one device copy of 512 MiB (a known-size kernel for "
                          "scaling hardware byte counters)")
@@ -264,7 +267,11 @@ def main():
     W_ = int(b.targets.shape[1])
     flags = 1 * (cu.dtype == torch.int64) | 2 * (ln.dtype == torch.int64) | 4 * (tg.dtype == torch.int64) \
         | 8 * (tl.dtype == torch.int64)
-    ws_bytes = api.packed_ctc_workspace_size(T_total, D, B, Umax, 1)
+    K = args.checkpoint_interval
+    ws_bytes = api.packed_ctc_workspace_size(T_total, D, B, Umax, K)
+    if ws_bytes == 0:
+        print(f"checkpoint interval {K} is not a power of two in [1, 32]", file=sys.stderr)
+        sys.exit(2)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     losses = torch.empty(B, dtype=torch.float32, device=dev)
     reduced = torch.empty((), dtype=torch.float32, device=dev)
@@ -274,7 +281,7 @@ def main():
     sh = ctypes.c_void_p(stream.cuda_stream)
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
     call_args = (P(lp), api.DTYPE_CODES[lp.dtype], T_total, D, P(cu), P(ln), B, P(tg), W_, P(tl), flags, Umax,
-                 b.blank, int(b.zero_infinity), red_code, None, P(losses), P(reduced), P(grad), 1, P(ws), ws_bytes, sh)
+                 b.blank, int(b.zero_infinity), red_code, None, P(losses), P(reduced), P(grad), K, P(ws), ws_bytes, sh)
 
     def step():
         rc = lib.packed_ctc_loss(*call_args)
@@ -367,7 +374,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": b.name, "B": B, "T_total": T_total, "D": D, "input_dtype": dname,
                    "max_target_length": Umax, "reduction": b.reduction, "zero_infinity": b.zero_infinity,
-                   "seed": "fixed"},
+                   "seed": "fixed", **({"checkpoint_interval": K} if K > 1 else {})},
         "call_hbm": {"achieved": call_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": call_gbps / HBM_PEAK_GBPS,
                      "counted_bytes": bytes_call},
         "phases_ms": phases,

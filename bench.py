@@ -237,7 +237,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (utterances would shard across "
+        print("bench.py measures one GPU: the library has no multi-GPU path (utterances would shard across "
               "GPUs with no exchange but a scalar all-reduce for sum/mean; see DESIGN.md). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)

@@ -64,7 +64,7 @@ extern "C" {
 #define PCTC_ERR_WORKSPACE 6          /* workspace missing or smaller than packed_ctc_workspace_size() */
 #define PCTC_ERR_HIP 7                /* a HIP runtime or launch error */
 #define PCTC_ERR_ARG 8                /* a required pointer is NULL, or an unknown flag / reduction */
-#define PCTC_ERR_LIMIT 9              /* beyond what this build supports (see packed_ctc_limits) */
+#define PCTC_ERR_LIMIT 9              /* beyond what the library supports (see packed_ctc_limits) */
 
 /* Pipelines of a packed_ctc_loss call that forms the gradient (packed_ctc_set_pipeline). */
 #define PCTC_PIPELINE_GROUPED 0   /* length-sorted groups on concurrent streams, rows after each group's recursions */
@@ -80,7 +80,7 @@ size_t packed_ctc_workspace_size(int64_t T_total, int64_t D, int64_t B, int64_t 
                                  int checkpoint_interval);
 
 /*
- * Supported maxima of this build: the longest target (labels) and the class count D.
+ * Supported maxima of the library: the longest target (labels) and the class count D.
  * Either pointer may be NULL.
  */
 void packed_ctc_limits(int64_t* max_target_length, int64_t* max_classes);
